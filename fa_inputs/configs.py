@@ -1,0 +1,62 @@
+"""The five workload definitions (shapes, types, value scales, seeds).
+
+Shapes and value distributions follow the attention workloads this library is
+measured on: self-attention with L_q = L_k = L, tensors laid out (B, H, L, d).
+Seeds are the workload index (0..4); streams 0/1/2 are Q/K/V.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+
+@dataclass(frozen=True)
+class Config:
+    index: int
+    name: str
+    B: int
+    H: int
+    L: int
+    d: int
+    dtype: int          # 0 = f32, 1 = f16, 2 = bf16 (storage of Q, K, V and O)
+    causal: int
+    scale: float
+    seed: int
+    sigma_q: float = 1.0
+    sigma_k: float = 1.0
+    sigma_v: float = 1.0
+    # number of query rows per (b, h) that the parity check compares against
+    # the oracle; None means every row
+    check_rows: int | None = None
+    notes: str = field(default="", compare=False)
+
+    @property
+    def flops(self) -> int:
+        """Metric FLOPs: 4*B*H*L^2*d, halved when causal."""
+        f = 4 * self.B * self.H * self.L * self.L * self.d
+        return f // 2 if self.causal else f
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once, O written once, lse (fp32) written once."""
+        eb = 4 if self.dtype == 0 else 2
+        n = self.B * self.H * self.L * self.d
+        return 4 * n * eb + 4 * self.B * self.H * self.L
+
+
+CONFIGS = [
+    Config(0, "single-head fp32 L256 d64", 1, 1, 256, 64, 0, 0, 1.0 / 8.0, 0,
+           notes="fp32 Q/K/V ~ N(0,1); tolerance 1e-5 relative"),
+    Config(1, "bf16 B4 H16 L1024 d64", 4, 16, 1024, 64, 2, 0, 1.0 / 8.0, 1),
+    Config(2, "bf16 causal B2 H32 L4096 d128", 2, 32, 4096, 128, 2, 1, 1.0 / math.sqrt(128.0), 2,
+           check_rows=256),
+    Config(3, "bf16 peaked B1 H32 L8192 d128", 1, 32, 8192, 128, 2, 0, 1.0 / math.sqrt(128.0), 3,
+           sigma_q=3.0, sigma_k=3.0, check_rows=256,
+           notes="Q, K ~ 3*N(0,1): score sigma ~ 9, peaked softmax"),
+    Config(4, "fp16 causal B1 H16 L16384 d64", 1, 16, 16384, 64, 1, 1, 1.0 / 8.0, 4,
+           check_rows=64, notes="oracle checked on 64 sampled query rows per head"),
+]
+
+
+def config(index: int) -> Config:
+    return CONFIGS[index]

@@ -1,0 +1,111 @@
+"""fp64 CPU oracle for the exact attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product library
+(``io_aware_tiled_02_amd``) never imports it, and this package never imports
+the product library: the two share no code.
+
+Contents
+  * ``fwd``   -- the plain definition (materialised score row, safe softmax,
+                 weighted sum, logsumexp) in C, float64, OpenMP over rows.
+  * ``brute`` -- a separate C brute-force twin for tiny shapes.
+  * ``tiled`` -- float64 NumPy models of the tiled online-softmax algorithm
+                 itself, used only to pin that the tiled method is exact.
+
+Every function here is pinned by the CPU tests against closed forms,
+invariants, library routines and values printed on the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (float64, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        lib.fa_oracle_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, d, i, vp, i, vp, vp, i]
+        lib.fa_oracle_fwd.restype = i
+        lib.fa_oracle_brute.argtypes = [vp, vp, vp, i, i, i, i, d, i, vp, vp]
+        lib.fa_oracle_brute.restype = i
+        lib.fa_oracle_max_threads.argtypes = []
+        lib.fa_oracle_max_threads.restype = i
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return _load().fa_oracle_max_threads()
+
+
+def _storage_check(a: np.ndarray, dtype: int) -> np.ndarray:
+    want = {0: np.float32, 1: np.float16, 2: np.uint16, 3: np.float64}[dtype]
+    if a.dtype != want:
+        raise TypeError(f"dtype code {dtype} expects storage {want}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def fwd(q, k, v, dtype: int, scale: float, causal: int, rows=None, nthreads: int = 0):
+    """O (B,H,nrows,d) and lse (B,H,nrows), float64, for the given query rows.
+
+    q, k, v: storage arrays (B, H, L, d) -- float32, float16, or uint16 holding
+    bfloat16 bits -- exactly as handed to the GPU library; dtype code 3 takes
+    float64 arrays (for the oracle's own pins).
+    """
+    q = _storage_check(q, dtype)
+    k = _storage_check(k, dtype)
+    v = _storage_check(v, dtype)
+    B, H, L, d = q.shape
+    if rows is None:
+        nrows, rows_arr, rows_ptr = L, None, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int32)
+        nrows = int(rows_arr.size)
+        rows_ptr = rows_arr.ctypes.data
+    o = np.empty((B, H, nrows, d), dtype=np.float64)
+    lse = np.empty((B, H, nrows), dtype=np.float64)
+    rc = _load().fa_oracle_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dtype,
+                               B, H, L, d, float(scale), int(causal), rows_ptr, nrows,
+                               o.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"fa_oracle_fwd rejected its arguments (rc={rc})")
+    return o, lse
+
+
+def brute(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: int):
+    """Brute-force O and lse from float64 (B,H,L,d) inputs; tiny shapes only."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, H, L, d = q.shape
+    o = np.empty((B, H, L, d), dtype=np.float64)
+    lse = np.empty((B, H, L), dtype=np.float64)
+    rc = _load().fa_oracle_brute(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                 B, H, L, d, float(scale), int(causal),
+                                 o.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"fa_oracle_brute rejected its arguments (rc={rc})")
+    return o, lse

@@ -1,0 +1,176 @@
+/*
+ * fp64 CPU oracle for the exact attention forward pass (definitions in
+ * fa_oracle.h).  TEST INFRASTRUCTURE ONLY: the product library never links
+ * or calls this file.  Plain C, no blocking, no fusion: each query row's full
+ * score row is materialised, then its maximum, its exponentials, their sum,
+ * the weighted sum of V and the logsumexp are computed in that order.
+ */
+#include "fa_oracle.h"
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* exact widening of one stored element to double */
+static double widen(const void* base, int dtype, size_t idx) {
+    if (dtype == ORACLE_F64) {
+        return ((const double*)base)[idx];
+    }
+    if (dtype == ORACLE_F32) {
+        return (double)((const float*)base)[idx];
+    }
+    if (dtype == ORACLE_BF16) {
+        /* bfloat16 is the upper half of a binary32 */
+        uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    /* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits */
+    uint16_t h = ((const uint16_t*)base)[idx];
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 10) & 0x1f;
+    int fr = h & 0x3ff;
+    double mag;
+    if (ex == 0) {
+        mag = ldexp((double)fr, -24);               /* zero or subnormal */
+    } else if (ex == 31) {
+        mag = fr ? NAN : INFINITY;
+    } else {
+        mag = ldexp((double)(fr + 1024), ex - 25);  /* (1 + fr/1024) * 2^(ex-15) */
+    }
+    return sign ? -mag : mag;
+}
+
+int fa_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+int fa_oracle_fwd(const void* q, const void* k, const void* v, int dtype,
+                  int B, int H, int L, int d, double scale, int causal,
+                  const int* rows, int nrows, double* o, double* lse, int nthreads) {
+    if (!q || !k || !v || !o || !lse) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16 && dtype != ORACLE_F64)
+        return -1;
+    if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || nrows <= 0) return -1;
+    if (causal != 0 && causal != 1) return -1;
+    if (!rows && nrows != L) return -1;
+    if (rows) {
+        for (int r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= L) return -1;
+    }
+    if (nthreads <= 0) nthreads = fa_oracle_max_threads();
+
+    const size_t head = (size_t)L * (size_t)d;
+    double* kd = (double*)malloc(head * sizeof(double));
+    double* vd = (double*)malloc(head * sizeof(double));
+    if (!kd || !vd) {
+        free(kd);
+        free(vd);
+        return -1;
+    }
+
+    for (int bh = 0; bh < B * H; ++bh) {
+        const size_t base = (size_t)bh * head;
+        for (size_t e = 0; e < head; ++e) {
+            kd[e] = widen(k, dtype, base + e);
+            vd[e] = widen(v, dtype, base + e);
+        }
+#pragma omp parallel num_threads(nthreads)
+        {
+            double* qi = (double*)malloc((size_t)d * sizeof(double));
+            double* s = (double*)malloc((size_t)L * sizeof(double));
+            double* p = (double*)malloc((size_t)L * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+            for (int r = 0; r < nrows; ++r) {
+                const int i = rows ? rows[r] : r;
+                for (int c = 0; c < d; ++c) qi[c] = widen(q, dtype, base + (size_t)i * d + c);
+
+                /* S row: scale * q_i . k_j ; causal keys after the query are -inf */
+                for (int j = 0; j < L; ++j) {
+                    if (causal && j > i) {
+                        s[j] = -INFINITY;
+                        continue;
+                    }
+                    double dot = 0.0;
+                    const double* kj = kd + (size_t)j * d;
+                    for (int c = 0; c < d; ++c) dot += qi[c] * kj[c];
+                    s[j] = scale * dot;
+                }
+                /* row maximum */
+                double m = -INFINITY;
+                for (int j = 0; j < L; ++j)
+                    if (s[j] > m) m = s[j];
+                /* exponentials relative to the maximum, and their sum */
+                double l = 0.0;
+                for (int j = 0; j < L; ++j) {
+                    p[j] = exp(s[j] - m);
+                    l += p[j];
+                }
+                /* O row = (P row . V) / l */
+                double* oi = o + ((size_t)bh * nrows + r) * d;
+                for (int c = 0; c < d; ++c) oi[c] = 0.0;
+                for (int j = 0; j < L; ++j) {
+                    const double* vj = vd + (size_t)j * d;
+                    for (int c = 0; c < d; ++c) oi[c] += p[j] * vj[c];
+                }
+                for (int c = 0; c < d; ++c) oi[c] /= l;
+                lse[(size_t)bh * nrows + r] = m + log(l);
+            }
+            free(qi);
+            free(s);
+            free(p);
+        }
+    }
+    free(kd);
+    free(vd);
+    return 0;
+}
+
+/* ---- brute-force twin: no shared helpers, every score recomputed ---- */
+
+static double brute_score(const double* qh, const double* kh, int d, double scale, int i, int j) {
+    double acc = 0.0;
+    for (int c = 0; c < d; ++c) acc += qh[(size_t)i * d + c] * kh[(size_t)j * d + c];
+    return acc * scale;
+}
+
+int fa_oracle_brute(const double* q, const double* k, const double* v,
+                    int B, int H, int L, int d, double scale, int causal,
+                    double* o, double* lse) {
+    if (!q || !k || !v || !o || !lse) return -1;
+    if (B <= 0 || H <= 0 || L <= 0 || d <= 0) return -1;
+    if (causal != 0 && causal != 1) return -1;
+    for (int bh = 0; bh < B * H; ++bh) {
+        const size_t off = (size_t)bh * L * d;
+        const double* qh = q + off;
+        const double* kh = k + off;
+        const double* vh = v + off;
+        for (int i = 0; i < L; ++i) {
+            const int last = causal ? i : L - 1;   /* keys 0..last are visible */
+            double mx = -INFINITY;
+            for (int j = 0; j <= last; ++j) {
+                double sc = brute_score(qh, kh, d, scale, i, j);
+                if (sc > mx) mx = sc;
+            }
+            double den = 0.0;
+            for (int j = 0; j <= last; ++j) den += exp(brute_score(qh, kh, d, scale, i, j) - mx);
+            for (int c = 0; c < d; ++c) {
+                double num = 0.0;
+                for (int j = 0; j <= last; ++j)
+                    num += exp(brute_score(qh, kh, d, scale, i, j) - mx) * vh[(size_t)j * d + c];
+                o[off + (size_t)i * d + c] = num / den;
+            }
+            lse[(size_t)bh * L + i] = mx + log(den);
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,65 @@
+/*
+ * fp64 CPU oracle for the exact attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this code; only the tests, the smoke check and the CPU-baseline leg of
+ * the bench use it.  It shares no code with the GPU library.
+ *
+ * What it computes is the plain definition of attention, not the tiled
+ * algorithm, because the tiled online-softmax method reaches exactly that
+ * result ("FlashAttention 深度解析", first article, section 3.4: the
+ * induction over K/V blocks; "FlashAttention: как реально считается attention
+ * на GPU": the tiled pass computes the same thing as ordinary attention).
+ * Per (batch, head) and query row i, in float64, from the stored inputs
+ * widened exactly:
+ *     s_ij  = scale * (q_i . k_j)            (j > i is -inf when causal)
+ *     m_i   = max_j s_ij
+ *     p_ij  = exp(s_ij - m_i)                (safe softmax, two passes)
+ *     l_i   = sum_j p_ij
+ *     o_i   = (sum_j p_ij v_j) / l_i
+ *     lse_i = m_i + ln(l_i)
+ * (standard attention: "FlashAttention 深度解析" first article section 2.3;
+ * safe softmax: "大语言模型研究14" section 1.1; logsumexp:
+ * "04 Transformers, Attention, and FlashAttention", FlashAttention-2
+ * Algorithm 1, the statistic L_i = m_i + log l_i.)
+ */
+#ifndef FA_ORACLE_H
+#define FA_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage type codes of q, k, v: 0 = float32, 1 = IEEE binary16, 2 = bfloat16,
+ * 3 = float64 (float64 exists for the oracle's own pins; the GPU library has
+ * no float64 path) */
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_F64 = 3 };
+
+/*
+ * q, k, v : host arrays (B, H, L, d), row-major, d fastest, in the storage type.
+ * rows    : host array of `nrows` query indices in [0, L) checked per (b, h);
+ *           NULL means every row (then nrows must equal L).
+ * o       : host float64 (B, H, nrows, d);  lse : host float64 (B, H, nrows).
+ * nthreads: OpenMP threads over rows (<= 0: the OpenMP default).
+ * Returns 0, or -1 on a bad argument (nothing written).
+ */
+int fa_oracle_fwd(const void* q, const void* k, const void* v, int dtype,
+                  int B, int H, int L, int d, double scale, int causal,
+                  const int* rows, int nrows, double* o, double* lse, int nthreads);
+
+/*
+ * Brute-force twin for tiny shapes: float64 inputs (B, H, L, d), and every
+ * score is recomputed from q and k wherever it is used (O(L^2 d^2)).
+ * Shares no helper with fa_oracle_fwd.  Returns 0, or -1 on a bad argument.
+ */
+int fa_oracle_brute(const double* q, const double* k, const double* v,
+                    int B, int H, int L, int d, double scale, int causal,
+                    double* o, double* lse);
+
+/* Threads an fa_oracle_fwd call with nthreads <= 0 would use. */
+int fa_oracle_max_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
