@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward pass on one MI355X.
+
+One step = one fa_fwd call over the whole workload (every step of the tiled
+online-softmax forward runs inside that one kernel launch).  Default workload:
+B=1, H=32, L=8192, d=128, bf16, non-causal, Q and K ~ 3*N(0,1), V ~ N(0,1)
+(the long non-causal head-dim-128 case the throughput target is quoted on).
+
+Prints ONE JSON line.  `value` is TFLOP/s counting 4*B*H*L^2*d FLOPs (half for
+causal) with inputs resident in HBM before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fa_inputs as gen  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s (4·B·H·L²·d) and % of MI355X bf16 MFMA peak"
+PEAK_TFLOPS = {gen.BF16: 2516.6, gen.F16: 2516.6, gen.F32: 157.3}   # dense MFMA peaks, MI355X
+KERNEL_SRC = os.path.join(ROOT, "io_aware_tiled_02_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_kernel.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_digest() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def traffic_for(workload_index: int):
+    """Measured HBM bytes per launch, if the counters were taken on this exact kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    if rec.get("kernel_source_sha256") != kernel_digest():
+        return None
+    w = rec.get("workloads", {}).get(str(workload_index))
+    if not w:
+        return None
+    return w["hbm_bytes_per_launch"]
+
+
+def cpu_baseline(cfg, q, k, v, target_s: float):
+    """The fp64 oracle timed on this host's cores over a bounded sample of query rows."""
+    import oracle
+    nth = oracle.max_threads()
+    per_row = 4.0 * cfg.L * cfg.d * (0.5 if cfg.causal else 1.0)   # metric FLOPs of one query row
+    rows0 = gen.sample_rows(cfg.L, min(16, cfg.L), cfg.seed)
+    t = time.perf_counter()
+    oracle.fwd(q, k, v, cfg.dtype, cfg.scale, cfg.causal, rows0)
+    t0 = max(time.perf_counter() - t, 1e-3)
+    nrows = int(min(cfg.L, max(16, rows0.size * target_s / t0)))
+    rows = gen.sample_rows(cfg.L, nrows, cfg.seed)
+    t = time.perf_counter()
+    oracle.fwd(q, k, v, cfg.dtype, cfg.scale, cfg.causal, rows)
+    dt = time.perf_counter() - t
+    flops = per_row * rows.size * cfg.B * cfg.H
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": nth,
+        "kind": "oracle",
+        "sample": (f"{rows.size} query rows per head x {cfg.B * cfg.H} heads of the same workload "
+                   f"(all L={cfg.L} keys each), fp64 C oracle, OpenMP; {dt:.1f} s"),
+        "seconds": dt,
+        "cpu_model": _cpu_model(),
+        "nproc": os.cpu_count(),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, help="workload index 0..4 (default 3)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(each GPU would run the same kernel on its own heads); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import io_aware_tiled_02_amd as fa
+
+    cfg = gen.config(args.workload)
+    log(f"[bench] workload {cfg.index}: {cfg.name}; generating inputs")
+    q, k, v = gen.make_qkv(cfg)
+
+    def dev(a):
+        if cfg.dtype == gen.BF16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(a).to("cuda")
+
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o = torch.empty_like(qd)
+    lse = torch.empty((cfg.B, cfg.H, cfg.L), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    call = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            cfg.B, cfg.H, cfg.L, cfg.d, float(cfg.scale), cfg.causal, cfg.dtype, sh)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        rc = fa.fa_fwd(*call)
+        if rc != 0:
+            raise SystemExit(f"fa_fwd failed: {rc} {fa.fa_strerror(rc)}")
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fa.fa_fwd(*call)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = cfg.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    log(f"[bench] {ms:.4f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak} TFLOP/s); "
+        f"wall {wall:.3f} s")
+
+    br, bc, wgs = fa.fa_fwd_tiling(cfg.B, cfg.H, cfg.L, cfg.d, cfg.causal, cfg.dtype)
+    traffic = traffic_for(cfg.index)
+    roofline = {
+        "bound": "mfma",
+        "achieved": tflops,
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": tflops / peak,
+        "traffic": traffic,
+        "kernel": "fa_fwd_kernel",
+        "per_launch_flops": cfg.flops,
+        "avg_launch_ms": ms,
+        "algorithmic_bytes_per_launch": cfg.algorithmic_bytes,
+    }
+    out = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": gen.DTYPE_NAMES[cfg.dtype],
+        "data": "synthetic (seeded SplitMix64 + Box-Muller normals, not torch.randn)",
+        "config": {
+            "workload": cfg.name,
+            "B": cfg.B, "H": cfg.H, "L": cfg.L, "d": cfg.d,
+            "causal": bool(cfg.causal),
+            "scale": cfg.scale,
+            "sigma_qkv": [cfg.sigma_q, cfg.sigma_k, cfg.sigma_v],
+            "block_rows": br, "block_cols": bc, "workgroups": wgs,
+            "pct_of_peak": 100.0 * tflops / peak,
+        },
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (fp64 oracle on a sample of rows)")
+        out["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

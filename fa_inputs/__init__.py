@@ -24,6 +24,9 @@ This is not torch.randn; values are i.i.d. N(0, sigma^2) up to the rounding.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .configs import CONFIGS, Config, config  # noqa: F401
@@ -36,7 +39,7 @@ _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _MIX1 = np.uint64(0xBF58476D1CE4E5B9)
 _MIX2 = np.uint64(0x94D049BB133111EB)
 _KEY_STREAM = np.uint64(0xD1B54A32D192ED03)
-_CHUNK = 1 << 22
+_CHUNK = 1 << 20
 
 
 def _key(seed: int, stream: int) -> np.uint64:
@@ -105,7 +108,7 @@ def fill(dtype: int, shape, seed: int, stream: int, sigma: float = 1.0) -> np.nd
         out = np.empty(n, dtype=np.uint16)
     else:
         raise ValueError(f"unknown dtype code {dtype}")
-    for s in range(0, n, _CHUNK):
+    def work(s):
         c = min(_CHUNK, n - s)
         v32 = normal(seed, stream, c, sigma, start=s).astype(np.float32)
         if dtype == F32:
@@ -114,6 +117,15 @@ def fill(dtype: int, shape, seed: int, stream: int, sigma: float = 1.0) -> np.nd
             out[s:s + c] = v32.astype(np.float16)
         else:
             out[s:s + c] = f32_to_bf16_bits(v32)
+
+    starts = range(0, n, _CHUNK)
+    if n > _CHUNK:
+        # chunks are independent (counter-based), so order does not matter
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(work, starts))
+    else:
+        for s in starts:
+            work(s)
     return out.reshape(shape)
 
 

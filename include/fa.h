@@ -1,0 +1,95 @@
+/*
+ * fa.h -- exact attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes; no C++ or framework types cross it.
+ *
+ * Operation (per batch b and head h, on one GPU):
+ *     S   = scale * Q K^T                      (L x L, never materialised)
+ *     S_ij = -inf for key j > query i          (only when causal = 1)
+ *     O   = softmax_rows(S) V                  (L x d)
+ *     lse_i = max_j S_ij + ln sum_j exp(S_ij - max_j S_ij)
+ * The definition is standard attention ("FlashAttention 深度解析", first
+ * article, section 2.3) with the causal mask of its second article, section
+ * 2.3 (a query attends to keys at or before its own position), and the
+ * logsumexp statistic L_i = m_i + log l_i that FlashAttention-2 Algorithm 1
+ * writes next to O ("04 Transformers, Attention, and FlashAttention").
+ * It is computed with the tiled online-softmax recurrence of that algorithm
+ * (running max m, running sum l, unnormalised output rescaled by
+ * exp(m_old - m_new) per K/V block, one division by l at the end), which is
+ * exact: the result equals the definition up to floating-point rounding.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of q, k, v and o.  lse is always float32. */
+enum fa_dtype {
+    FA_F32 = 0,   /* IEEE binary32; the products and P stay in fp32       */
+    FA_F16 = 1,   /* IEEE binary16; fp32 accumulation, P rounded to fp16  */
+    FA_BF16 = 2   /* bfloat16;      fp32 accumulation, P rounded to bf16  */
+};
+
+/* Return codes.  0 is success; every failure is negative. */
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1,  /* null pointer; B, H or L <= 0; scale not finite or <= 0;
+                                 causal not 0/1; B*H*L*d >= 2^62; too many Q tiles for one grid */
+    FA_ERR_UNSUPPORTED = -2,  /* d not 64 or 128; unknown dtype                              */
+    FA_ERR_ALIGN = -3,        /* q, k, v or o not 16-byte aligned; lse not 4-byte aligned   */
+    FA_ERR_HIP = -4           /* the kernel launch failed; see fa_last_hip_error()          */
+};
+
+/*
+ * fa_fwd -- enqueue the forward pass on `stream` and return.
+ *
+ * q, k, v : device pointers, read only, each (B, H, L, d) contiguous row-major
+ *           with d fastest: element (b, h, l, c) at ((b*H + h)*L + l)*d + c.
+ * o       : device pointer, (B, H, L, d) in the same layout and type; fully
+ *           overwritten.  Must not overlap q, k, v or lse.
+ * lse     : device pointer, float32 (B, H, L) contiguous; fully overwritten
+ *           with the natural-log logsumexp of each scaled score row.
+ * B, H, L : batch, heads, sequence length (L_q = L_k = L).
+ * d       : head dimension, 64 or 128.
+ * scale   : multiplies Q K^T before the softmax (1/sqrt(d) in the usual form);
+ *           finite and > 0.
+ * causal  : 0 = full attention; 1 = key j > query i is masked out.
+ * dtype   : an fa_dtype value.
+ * stream  : HIP stream (0 = the null stream).
+ *
+ * Ownership: the caller owns all five buffers.  The library allocates and
+ * frees nothing, copies nothing to or from the host, never synchronises, and
+ * keeps no state between calls; calls are thread-safe and reentrant.
+ * Results are valid once `stream` has reached this work.
+ *
+ * Errors: argument errors are detected on the host before anything is
+ * enqueued (no partial writes) and return FA_ERR_INVALID_ARG,
+ * FA_ERR_UNSUPPORTED or FA_ERR_ALIGN.  A launch failure returns FA_ERR_HIP and
+ * records the HIP error code for fa_last_hip_error().  NaN or Inf inputs are
+ * not errors: they propagate through the arithmetic.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int L, int d, float scale, int causal, int dtype,
+           hipStream_t stream);
+
+/* Static description of a return code (never NULL). */
+const char* fa_strerror(int status);
+
+/* HIP error code of the last FA_ERR_HIP returned on the calling thread
+ * (hipSuccess if none). */
+int fa_last_hip_error(void);
+
+/* Query-tile height B_r and key-tile width B_c that fa_fwd uses for a
+ * (d, causal, dtype) combination, and the number of workgroups it launches
+ * for (B, H, L).  Returns FA_OK or an argument error as fa_fwd would. */
+int fa_fwd_tiling(int B, int H, int L, int d, int causal, int dtype,
+                  int* block_rows, int* block_cols, long long* workgroups);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA_H */

@@ -1,0 +1,103 @@
+"""Exact attention forward pass for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding of the C ABI declared in include/fa.h and implemented
+by the in-tree HIP library libfa_fwd.so.  Every step of the computation runs
+in that library's kernels; this module only marshals arguments.  PyTorch is
+used for device memory and streams.  There is no fallback: if the library is
+missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_HIP = 0, -1, -2, -3, -4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"fa_fwd failed: {code} ({msg})")
+        self.code = code
+
+
+def load():
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (__graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+        lib.fa_fwd.restype = i
+        lib.fa_strerror.argtypes = [i]
+        lib.fa_strerror.restype = ctypes.c_char_p
+        lib.fa_last_hip_error.argtypes = []
+        lib.fa_last_hip_error.restype = i
+        lib.fa_fwd_tiling.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
+                                      ctypes.POINTER(ctypes.c_longlong)]
+        lib.fa_fwd_tiling.restype = i
+        _lib = lib
+    return _lib
+
+
+def fa_fwd(q, k, v, o, lse, B, H, L, d, scale, causal, dtype, stream) -> int:
+    """The C entry point as is: raw device addresses (ints) and a raw stream handle."""
+    return load().fa_fwd(q, k, v, o, lse, B, H, L, d, scale, causal, dtype, stream)
+
+
+def fa_strerror(code: int) -> str:
+    return load().fa_strerror(code).decode()
+
+
+def fa_last_hip_error() -> int:
+    return load().fa_last_hip_error()
+
+
+def fa_fwd_tiling(B, H, L, d, causal, dtype):
+    """(block_rows, block_cols, workgroups) that fa_fwd uses for this shape."""
+    br, bc, wg = ctypes.c_int(), ctypes.c_int(), ctypes.c_longlong()
+    rc = load().fa_fwd_tiling(B, H, L, d, causal, dtype, ctypes.byref(br), ctypes.byref(bc), ctypes.byref(wg))
+    if rc != FA_OK:
+        raise FAError(rc, fa_strerror(rc))
+    return br.value, bc.value, wg.value
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def forward(q, k, v, scale: float, causal: bool = False, out=None, lse=None, stream=None):
+    """O and lse for torch device tensors q, k, v of shape (B, H, L, d).
+
+    Outputs are allocated with torch unless given.  The work is enqueued on
+    `stream` (default: torch's current stream) and not waited for.
+    """
+    import torch
+    if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
+        raise ValueError("q, k, v must share one (B, H, L, d) shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, L, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H, L, d, float(scale), int(bool(causal)), _dtype_code(q), stream.cuda_stream)
+    if rc != FA_OK:
+        raise FAError(rc, fa_strerror(rc))
+    return out, lse

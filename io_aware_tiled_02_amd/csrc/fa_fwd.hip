@@ -1,0 +1,606 @@
+// Exact attention forward pass for gfx950 (MI355X, CDNA4).
+//
+// One workgroup owns one (batch, head, B_r-row query tile) and streams every
+// K/V tile of that head through LDS once, keeping per query row a running
+// maximum m, a running sum l and an unnormalised output accumulator, all in
+// fp32 registers.  Per K/V tile j:
+//     S      = Q_i K_j^T                          (MFMA, fp32 accumulate)
+//     m_new  = max(m, rowmax S)
+//     P      = exp(scale*S - scale*m_new)         (computed as exp2)
+//     l      = exp(scale*(m - m_new)) * l + rowsum P
+//     O      = exp(scale*(m - m_new)) * O + P V_j (MFMA, P rounded to T)
+// and after the last tile O /= l, lse = scale*m + ln l.  This is Algorithm 1
+// of FlashAttention-2 ("04 Transformers, Attention, and FlashAttention":
+// Q blocks outer and parallel, K/V blocks inner and serial, one division at
+// the end, L_i = m_i + log l_i), the row-block recurrence of
+// "大语言模型研究14" section 2, and the causal block skipping of
+// "FlashAttention 深度解析" (second article, section 2.3).
+//
+// gfx950 mapping
+//  * Each wavefront owns QPW = 32*NQB query rows and does every step for them
+//    alone, so no row statistic is ever combined across waves.
+//  * The score tile is computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_{bf16,f16}: in the 32x32 accumulator layout a lane
+//    holds ONE query (its column) and 16 keys, so the row max and row sum are
+//    plain in-register max/add chains plus one exchange with lane^32.
+//  * The output is accumulated transposed too, O^T += V^T P^T: the P values a
+//    lane holds are exactly the B operand it needs, so P never leaves
+//    registers.  V is written to LDS transposed (d-major), with the 32-key
+//    sub-tile's key positions permuted so that each lane's 8 keys are one
+//    contiguous 16-byte read.
+//  * K and V^T tiles are double-buffered in LDS; tile j+1 is fetched from HBM
+//    into registers with 16-byte loads while tile j is computed.
+//  * 16-byte LDS chunks are XOR-swizzled by row to spread banks.
+//  * Workgroups are renumbered so that every query tile of a head runs on the
+//    same XCD (they share that head's K/V in the XCD's L2); causal tiles are
+//    issued heaviest first.
+//  * The fp32 type uses the same data path with v_mfma_f32_32x32x2f32 and
+//    keeps P in fp32.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- per storage type: fragment of 8 k-values per lane, and the MFMA step ----
+template <class T>
+struct Ty;
+
+template <>
+struct Ty<__bf16> {
+    using frag = bf16x8;
+    static constexpr int kBytes = 2;
+    __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline frag cvt(const float* x) {
+        frag r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
+        return r;
+    }
+};
+
+template <>
+struct Ty<_Float16> {
+    using frag = f16x8;
+    static constexpr int kBytes = 2;
+    __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline frag cvt(const float* x) {
+        frag r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = (_Float16)x[e];
+        return r;
+    }
+};
+
+template <>
+struct Ty<float> {
+    using frag = f32x8;
+    static constexpr int kBytes = 4;
+    // eight k=2 steps; element e of every lane's fragment feeds step e, so
+    // both operands see the same k order
+    __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
+        return c;
+    }
+    __device__ static inline frag cvt(const float* x) {
+        frag r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = x[e];
+        return r;
+    }
+};
+
+// 16-byte global / LDS accesses
+__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline void st16(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
+__device__ inline void st8(void* p, u32x2 x) { *reinterpret_cast<u32x2*>(p) = x; }
+
+// Position of key k (0..31) of a 32-key sub-tile inside a transposed V row.
+// The S^T accumulator register r of lane half h holds key 8*(r/4) + 4h + r%4;
+// PV step p consumes registers 8p..8p+7.  Swapping bits 2 and 3 of the key
+// makes those 8 keys the contiguous positions 16p + 8h .. 16p + 8h + 7.
+__device__ inline int vpos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+struct Params {
+    const char* q;
+    const char* k;
+    const char* v;
+    char* o;
+    float* lse;
+    int L;
+    int BH;
+    int Tr;       // query tiles per head
+    int remap;    // 1: BH % 8 == 0, keep a head's tiles on one XCD
+    float c;      // scale * log2(e)
+    float scale;
+};
+
+template <class T, int D, bool CAUSAL, int NQB, int NW, int NKB>
+struct Cfg {
+    static constexpr int E = Ty<T>::kBytes;
+    static constexpr int QPW = 32 * NQB;          // query rows per wave
+    static constexpr int BR = NW * QPW;           // query rows per workgroup
+    static constexpr int BC = 32 * NKB;           // keys per K/V tile
+    static constexpr int NT = NW * 64;            // threads
+    static constexpr int EPC = 16 / E;            // elements per 16-byte chunk
+    static constexpr int KCPR = D / EPC;          // chunks per K row (= per V row in HBM)
+    static constexpr int VCPR = BC / EPC;         // chunks per transposed-V row
+    static constexpr int KSW = (KCPR >= 8 ? 8 : KCPR) - 1;
+    static constexpr int VSW = (VCPR >= 8 ? 8 : VCPR) - 1;
+    static constexpr int KBYTES = BC * D * E;
+    static constexpr int VBYTES = D * BC * E;
+    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int KUNITS = BC * KCPR;      // 16-byte pieces of a K tile
+    static constexpr int KPT = KUNITS / NT;       // per thread
+    static constexpr int VUNITS = (BC / 4) * KCPR;   // (4 keys x 16 bytes) pieces of a V tile
+    static constexpr int VPT = (VUNITS + NT - 1) / NT;
+    static_assert(KUNITS % NT == 0, "K tile must split evenly over the threads");
+    static_assert(D % 32 == 0 && BC % 32 == 0, "tile shapes");
+    static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
+};
+
+__device__ inline int vswz(int row, int mask) { return (row ^ (row >> 3)) & mask; }
+
+template <class T, int D, bool CAUSAL, int NQB, int NW, int NKB>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+__attribute__((amdgpu_waves_per_eu(NQB == 1 ? 2 : 1, NQB == 1 ? 2 : 1)))
+void fa_fwd_kernel(Params p) {
+    using C = Cfg<T, D, CAUSAL, NQB, NW, NKB>;
+    using frag = typename Ty<T>::frag;
+    constexpr int E = C::E;
+    constexpr int BC = C::BC;
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+
+    // ---- which (head, query tile) this workgroup owns ----
+    const int w = blockIdx.x;
+    int bh, qt;
+    if (p.remap) {
+        const int xcd = w & 7, s = w >> 3, hp = p.BH >> 3;
+        if (CAUSAL) {
+            qt = p.Tr - 1 - s / hp;
+            bh = xcd * hp + s % hp;
+        } else {
+            bh = xcd * hp + s / p.Tr;
+            qt = s % p.Tr;
+        }
+    } else if (CAUSAL) {
+        qt = p.Tr - 1 - w / p.BH;
+        bh = w % p.BH;
+    } else {
+        bh = w / p.Tr;
+        qt = w % p.Tr;
+    }
+
+    const int L = p.L;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hf = lane >> 5;
+    const long long head = (long long)bh * L * D;   // element offset of this head
+    const char* qh = p.q + head * E;
+    const char* kh = p.k + head * E;
+    const char* vh = p.v + head * E;
+
+    const int q0 = qt * C::BR;
+    const int qw = q0 + wave * C::QPW;                 // first query row of this wave
+    const int qend = min(q0 + C::BR, L);
+    const int ntiles = CAUSAL ? (qend + BC - 1) / BC : (L + BC - 1) / BC;
+
+    // ---- Q fragments: B operand of S^T = K Q^T, lane = query, 8 d-values ----
+    frag qf[NQB][D / 16];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int row = qw + qb * 32 + l32;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            u32x4 raw[E / 2];
+#pragma unroll
+            for (int x = 0; x < E / 2; ++x) {
+                raw[x] = u32x4{0, 0, 0, 0};
+                if (row < L) raw[x] = ld16(qh + ((long long)row * D + 16 * s + 8 * hf) * E + 16 * x);
+            }
+            qf[qb][s] = __builtin_bit_cast(frag, raw);
+        }
+    }
+
+    // ---- K/V tile prefetch registers ----
+    u32x4 kr[C::KPT];
+    u32x4 vr[C::VPT][4];
+
+    auto fetch = [&](int j) {
+        const int kb = j * BC;
+#pragma unroll
+        for (int x = 0; x < C::KPT; ++x) {
+            const int u = tid + x * C::NT;
+            const int row = u / C::KCPR, c = u % C::KCPR;
+            const int key = kb + row;
+            kr[x] = u32x4{0, 0, 0, 0};
+            if (key < L) kr[x] = ld16(kh + ((long long)key * D) * E + 16 * c);
+        }
+#pragma unroll
+        for (int x = 0; x < C::VPT; ++x) {
+            const int u = tid + x * C::NT;
+            const int a = u / C::KCPR, c = u % C::KCPR;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = kb + 4 * a + e;
+                vr[x][e] = u32x4{0, 0, 0, 0};
+                if (u < C::VUNITS && key < L) vr[x][e] = ld16(vh + ((long long)key * D) * E + 16 * c);
+            }
+        }
+    };
+
+    auto stash = [&](int stage) {
+        char* ks = smem + stage * C::STAGE;
+        char* vs = ks + C::KBYTES;
+#pragma unroll
+        for (int x = 0; x < C::KPT; ++x) {
+            const int u = tid + x * C::NT;
+            const int row = u / C::KCPR, c = u % C::KCPR;
+            st16(ks + row * (D * E) + ((c ^ (row & C::KSW)) * 16), kr[x]);
+        }
+#pragma unroll
+        for (int x = 0; x < C::VPT; ++x) {
+            const int u = tid + x * C::NT;
+            if (u >= C::VUNITS) continue;
+            const int a = u / C::KCPR, c = u % C::KCPR;
+            const int key4 = 4 * a;                             // 4 consecutive keys
+            const int pos = (key4 & ~31) | vpos(key4 & 31);     // their position (contiguous 4)
+            const int byte = pos * E;
+#pragma unroll
+            for (int dd = 0; dd < C::EPC; ++dd) {
+                const int drow = c * C::EPC + dd;
+                char* dst = vs + drow * (BC * E) + (((byte >> 4) ^ vswz(drow, C::VSW)) << 4) + (byte & 15);
+                if constexpr (E == 2) {
+                    const int wi = dd >> 1;
+                    uint32_t x0 = vr[x][0][wi], x1 = vr[x][1][wi], x2 = vr[x][2][wi], x3 = vr[x][3][wi];
+                    u32x2 out;
+                    if (dd & 1) {
+                        out[0] = (x0 >> 16) | (x1 & 0xffff0000u);
+                        out[1] = (x2 >> 16) | (x3 & 0xffff0000u);
+                    } else {
+                        out[0] = (x0 & 0xffffu) | (x1 << 16);
+                        out[1] = (x2 & 0xffffu) | (x3 << 16);
+                    }
+                    st8(dst, out);
+                } else {
+                    st16(dst, u32x4{vr[x][0][dd], vr[x][1][dd], vr[x][2][dd], vr[x][3][dd]});
+                }
+            }
+        }
+    };
+
+    // ---- running statistics (per lane: one query per qb) and accumulators ----
+    float m_raw[NQB], mc[NQB], lsum[NQB];
+    f32x16 oacc[NQB][D / 32];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        m_raw[qb] = -INFINITY;
+        mc[qb] = -INFINITY;
+        lsum[qb] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][dt][r] = 0.f;
+    }
+
+    fetch(0);
+    stash(0);
+    __syncthreads();
+
+    for (int j = 0; j < ntiles; ++j) {
+        if (j + 1 < ntiles) fetch(j + 1);
+
+        const char* ks = smem + (j & 1) * C::STAGE;
+        const char* vs = ks + C::KBYTES;
+        const int kb = j * BC;
+        // a wave whose rows all precede this tile has nothing to do in it
+        const bool active = !CAUSAL || kb <= qw + C::QPW - 1;
+        const bool need_mask = (kb + BC > L) || (CAUSAL && kb + BC - 1 > qw);
+
+        if (active) {
+            // S^T = K_j Q^T : lane = query, registers = keys
+            f32x16 sacc[NQB][NKB];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[qb][kt][r] = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < NKB; ++kt) {
+                const int row = kt * 32 + l32;
+                const char* krow = ks + row * (D * E);
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) {
+                    u32x4 raw[E / 2];
+#pragma unroll
+                    for (int x = 0; x < E / 2; ++x) {
+                        const int c = ((16 * s + 8 * hf) * E) / 16 + x;
+                        raw[x] = ld16(krow + ((c ^ (row & C::KSW)) * 16));
+                    }
+                    const frag a = __builtin_bit_cast(frag, raw);
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) sacc[qb][kt] = Ty<T>::mma(a, qf[qb][s], sacc[qb][kt]);
+                }
+            }
+
+            if (need_mask) {
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    const int query = qw + qb * 32 + l32;
+#pragma unroll
+                    for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = kb + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+                            if (key >= L || (CAUSAL && key > query)) sacc[qb][kt][r] = -INFINITY;
+                        }
+                }
+            }
+
+            // online softmax update, one query row per lane and qb
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                float mx = sacc[qb][0][0];
+#pragma unroll
+                for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kt][r]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float m_new = fmaxf(m_raw[qb], mx);
+                // reference for the exponent; 0 while the row has seen no key
+                const float ref = (m_new == -INFINITY) ? 0.f : m_new * p.c;
+                const float alpha = __builtin_amdgcn_exp2f(mc[qb] - ref);
+                m_raw[qb] = m_new;
+                mc[qb] = ref;
+                float ls = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kt][r], p.c, -ref));
+                        sacc[qb][kt][r] = e;
+                        ls += e;
+                    }
+                lsum[qb] = alpha * lsum[qb] + ls;
+                if (__ballot(alpha != 1.f)) {
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[qb][dt][r] *= alpha;
+                }
+            }
+
+            // O^T += V_j^T P^T
+#pragma unroll
+            for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+                for (int ps = 0; ps < 2; ++ps) {
+                    frag pb[NQB];
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) {
+                        float tmp[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) tmp[e] = sacc[qb][kt][8 * ps + e];
+                        pb[qb] = Ty<T>::cvt(tmp);
+                    }
+                    const int kpos = kt * 32 + 16 * ps + 8 * hf;   // first of this lane's 8 keys
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt) {
+                        const int drow = dt * 32 + l32;
+                        const char* vrow = vs + drow * (BC * E);
+                        u32x4 raw[E / 2];
+#pragma unroll
+                        for (int x = 0; x < E / 2; ++x) {
+                            const int c = (kpos * E) / 16 + x;
+                            raw[x] = ld16(vrow + ((c ^ vswz(drow, C::VSW)) * 16));
+                        }
+                        const frag a = __builtin_bit_cast(frag, raw);
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb) oacc[qb][dt] = Ty<T>::mma(a, pb[qb], oacc[qb][dt]);
+                    }
+                }
+        }
+
+        if (j + 1 < ntiles) stash((j + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: one division by l, logsumexp, stores ----
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
+        const float inv = 1.f / ltot;
+        const int query = qw + qb * 32 + l32;
+        if (query < L) {
+            char* orow = p.o + (head + (long long)query * D) * E;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = dt * 32 + g * 8 + hf * 4;
+                    if constexpr (E == 2) {
+                        T o4[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[qb][dt][4 * g + e] * inv);
+                        st8(orow + col * E, __builtin_bit_cast(u32x2, o4));
+                    } else {
+                        float o4[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o4[e] = oacc[qb][dt][4 * g + e] * inv;
+                        st16(orow + col * E, __builtin_bit_cast(u32x4, o4));
+                    }
+                }
+            if (hf == 0) p.lse[(long long)bh * L + query] = (mc[qb] + __builtin_amdgcn_logf(ltot)) * kLn2;
+        }
+    }
+}
+
+// ---- host side ----
+
+thread_local int g_last_hip = 0;
+
+struct Tiling {
+    int br, bc;
+};
+
+template <class T, int D, bool CAUSAL>
+struct Choice;
+// bf16 / fp16: 4 waves x 32 rows, 64-key tiles
+template <int D, bool CAUSAL>
+struct Choice<__bf16, D, CAUSAL> {
+    static constexpr int NQB = 1, NW = 4, NKB = 2;
+};
+template <int D, bool CAUSAL>
+struct Choice<_Float16, D, CAUSAL> {
+    static constexpr int NQB = 1, NW = 4, NKB = 2;
+};
+// fp32: 64-key tiles at d = 64, 32-key tiles at d = 128 (LDS budget)
+template <int D, bool CAUSAL>
+struct Choice<float, D, CAUSAL> {
+    static constexpr int NQB = 1, NW = 4, NKB = (D == 64 ? 2 : 1);
+};
+
+template <class T, int D, bool CAUSAL>
+Tiling tiling_of() {
+    using Ch = Choice<T, D, CAUSAL>;
+    using C = Cfg<T, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>;
+    return Tiling{C::BR, C::BC};
+}
+
+template <class T, int D, bool CAUSAL>
+int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int L, float scale,
+           hipStream_t stream) {
+    using Ch = Choice<T, D, CAUSAL>;
+    using C = Cfg<T, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>;
+    Params p;
+    p.q = static_cast<const char*>(q);
+    p.k = static_cast<const char*>(k);
+    p.v = static_cast<const char*>(v);
+    p.o = static_cast<char*>(o);
+    p.lse = lse;
+    p.L = L;
+    p.BH = BH;
+    p.Tr = (L + C::BR - 1) / C::BR;
+    p.remap = (BH % 8 == 0) ? 1 : 0;
+    p.c = scale * kLog2e;
+    p.scale = scale;
+    const long long grid = (long long)BH * p.Tr;
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>), dim3((unsigned)grid),
+                       dim3(C::NT), 0, stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+        g_last_hip = (int)err;
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+}
+
+template <class T>
+Tiling tiling_for(int d, int causal) {
+    if (d == 64) return causal ? tiling_of<T, 64, true>() : tiling_of<T, 64, false>();
+    return causal ? tiling_of<T, 128, true>() : tiling_of<T, 128, false>();
+}
+
+Tiling tiling_dispatch(int d, int causal, int dtype) {
+    if (dtype == FA_F32) return tiling_for<float>(d, causal);
+    if (dtype == FA_F16) return tiling_for<_Float16>(d, causal);
+    return tiling_for<__bf16>(d, causal);
+}
+
+int check_args(int B, int H, int L, int d, int causal, int dtype) {
+    if (B <= 0 || H <= 0 || L <= 0) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    const long long n = (long long)B * H * L;
+    if (n >= (1LL << 62) / d) return FA_ERR_INVALID_ARG;
+    const Tiling t = tiling_dispatch(d, causal, dtype);
+    const long long grid = (long long)B * H * ((L + t.br - 1) / t.br);
+    if (grid > 0x7fffffffLL || (long long)B * H > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int L,
+                      int d, float scale, int causal, int dtype, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    const int rc = check_args(B, H, L, d, causal, dtype);
+    if (rc != FA_OK) return rc;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
+    if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;
+    const int BH = B * H;
+    if (dtype == FA_BF16) {
+        if (d == 64)
+            return causal ? launch<__bf16, 64, true>(q, k, v, o, lse, BH, L, scale, stream)
+                          : launch<__bf16, 64, false>(q, k, v, o, lse, BH, L, scale, stream);
+        return causal ? launch<__bf16, 128, true>(q, k, v, o, lse, BH, L, scale, stream)
+                      : launch<__bf16, 128, false>(q, k, v, o, lse, BH, L, scale, stream);
+    }
+    if (dtype == FA_F16) {
+        if (d == 64)
+            return causal ? launch<_Float16, 64, true>(q, k, v, o, lse, BH, L, scale, stream)
+                          : launch<_Float16, 64, false>(q, k, v, o, lse, BH, L, scale, stream);
+        return causal ? launch<_Float16, 128, true>(q, k, v, o, lse, BH, L, scale, stream)
+                      : launch<_Float16, 128, false>(q, k, v, o, lse, BH, L, scale, stream);
+    }
+    if (d == 64)
+        return causal ? launch<float, 64, true>(q, k, v, o, lse, BH, L, scale, stream)
+                      : launch<float, 64, false>(q, k, v, o, lse, BH, L, scale, stream);
+    return causal ? launch<float, 128, true>(q, k, v, o, lse, BH, L, scale, stream)
+                  : launch<float, 128, false>(q, k, v, o, lse, BH, L, scale, stream);
+}
+
+extern "C" const char* fa_strerror(int status) {
+    switch (status) {
+        case FA_OK:
+            return "success";
+        case FA_ERR_INVALID_ARG:
+            return "invalid argument (null pointer, non-positive size, bad scale or causal flag, or size overflow)";
+        case FA_ERR_UNSUPPORTED:
+            return "unsupported head dimension (64 or 128) or dtype (0 f32, 1 f16, 2 bf16)";
+        case FA_ERR_ALIGN:
+            return "misaligned pointer (q, k, v, o need 16 bytes; lse needs 4)";
+        case FA_ERR_HIP:
+            return "HIP kernel launch failed (see fa_last_hip_error)";
+        default:
+            return "unknown status";
+    }
+}
+
+extern "C" int fa_last_hip_error(void) { return g_last_hip; }
+
+extern "C" int fa_fwd_tiling(int B, int H, int L, int d, int causal, int dtype, int* block_rows, int* block_cols,
+                             long long* workgroups) {
+    const int rc = check_args(B, H, L, d, causal, dtype);
+    if (rc != FA_OK) return rc;
+    const Tiling t = tiling_dispatch(d, causal, dtype);
+    if (block_rows) *block_rows = t.br;
+    if (block_cols) *block_cols = t.bc;
+    if (workgroups) *workgroups = (long long)B * H * ((L + t.br - 1) / t.br);
+    return FA_OK;
+}

@@ -1,0 +1,192 @@
+"""GPU parity: fa_fwd through the C ABI against the fp64 oracle.
+
+Every case names itself on stdout before it touches the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs as gen
+import oracle
+from parity_util import compare, run_gpu, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import io_aware_tiled_02_amd as fa
+    fa.load()
+
+
+# ---- the five workloads at full size -----------------------------------------
+
+@pytest.mark.parametrize("idx", range(5))
+def test_workload_parity(idx):
+    cfg = gen.config(idx)
+    say(f"[parity] workload {idx}: {cfg.name} B={cfg.B} H={cfg.H} L={cfg.L} d={cfg.d} "
+        f"dtype={gen.DTYPE_NAMES[cfg.dtype]} causal={cfg.causal}")
+    q, k, v = gen.make_qkv(cfg)
+    o, lse = run_gpu(q, k, v, cfg.dtype, cfg.scale, cfg.causal)
+    rows = None if cfg.check_rows is None else gen.sample_rows(cfg.L, cfg.check_rows, cfg.seed)
+    o_ref, lse_ref = oracle.fwd(q, k, v, cfg.dtype, cfg.scale, cfg.causal, rows)
+    if rows is not None:
+        o, lse = o[:, :, rows], lse[:, :, rows]
+        say(f"[parity] workload {idx}: checked rows {rows.tolist()}")
+    stats = compare(o, lse, o_ref, lse_ref, cfg.dtype, f"workload {idx}")
+    say(f"[parity] workload {idx}: {stats}")
+
+
+# ---- small shapes: several tiles, ragged tails, both head sizes and masks ----
+
+EDGE_L = [1, 2, 17, 63, 64, 65, 127, 129, 300, 1000]
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.F16, gen.F32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_edge_shapes(dtype, d, causal):
+    for L in EDGE_L:
+        B, H = 1, 3
+        say(f"[edge] dtype={gen.DTYPE_NAMES[dtype]} d={d} causal={causal} L={L}")
+        shape = (B, H, L, d)
+        seed = 1000 + L
+        q = gen.fill(dtype, shape, seed, 0, 1.5)
+        k = gen.fill(dtype, shape, seed, 1, 1.5)
+        v = gen.fill(dtype, shape, seed, 2)
+        scale = 1.0 / math.sqrt(d)
+        o, lse = run_gpu(q, k, v, dtype, scale, causal)
+        o_ref, lse_ref = oracle.fwd(q, k, v, dtype, scale, causal)
+        compare(o, lse, o_ref, lse_ref, dtype, f"L={L} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_xcd_remap_many_heads(causal):
+    """B*H a multiple of 8 (heads grouped per XCD) with a ragged last Q tile."""
+    B, H, L, d, dtype = 2, 8, 700, 64, gen.BF16
+    say(f"[remap] B={B} H={H} L={L} causal={causal}")
+    shape = (B, H, L, d)
+    q = gen.fill(dtype, shape, 77, 0)
+    k = gen.fill(dtype, shape, 77, 1)
+    v = gen.fill(dtype, shape, 77, 2)
+    o, lse = run_gpu(q, k, v, dtype, 0.125, causal)
+    o_ref, lse_ref = oracle.fwd(q, k, v, dtype, 0.125, causal)
+    compare(o, lse, o_ref, lse_ref, dtype, "remap")
+
+
+# ---- the teaching check's shape at its own tolerance (fp32) -------------------
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_equivalence_shape_fp32(causal):
+    B, H, L, d = 2, 4, 128, 64
+    say(f"[equiv] fp32 B={B} H={H} L={L} d={d} causal={causal}")
+    shape = (B, H, L, d)
+    q = gen.fill(gen.F32, shape, 42, 0)
+    k = gen.fill(gen.F32, shape, 42, 1)
+    v = gen.fill(gen.F32, shape, 42, 2)
+    o, lse = run_gpu(q, k, v, gen.F32, 1.0 / 8.0, causal)
+    o_ref, _ = oracle.fwd(q, k, v, gen.F32, 1.0 / 8.0, causal)
+    assert np.max(np.abs(o - o_ref)) < 1e-5
+
+
+# ---- closed forms on the GPU --------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.F16])
+def test_constant_keys_give_mean_of_v(dtype):
+    B, H, L, d = 1, 2, 512, 128
+    say(f"[closed] constant K dtype={gen.DTYPE_NAMES[dtype]}")
+    q = gen.fill(dtype, (B, H, L, d), 5, 0)
+    krow = gen.fill(dtype, (B, H, 1, d), 5, 1)
+    k = np.ascontiguousarray(np.broadcast_to(krow, (B, H, L, d)))
+    v = gen.fill(dtype, (B, H, L, d), 5, 2)
+    for causal in (0, 1):
+        o, lse = run_gpu(q, k, v, dtype, 0.1, causal)
+        vf = gen.to_float64(v, dtype)
+        n = np.arange(1, L + 1)[None, None, :, None] if causal else L
+        mean = (np.cumsum(vf, axis=2) / n) if causal else np.broadcast_to(vf.mean(axis=2, keepdims=True), vf.shape)
+        assert np.max(np.abs(o - mean)) <= 2e-2
+        qk = 0.1 * np.einsum("bhld,bhd->bhl", gen.to_float64(q, dtype), gen.to_float64(krow, dtype)[:, :, 0])
+        cnt = np.arange(1, L + 1) if causal else L
+        np.testing.assert_allclose(lse, qk + np.log(cnt), atol=1e-3)
+
+
+def test_dominant_score_selects_value_row():
+    B, H, L, d, dtype = 1, 1, 256, 64, gen.BF16
+    say("[closed] dominant score")
+    q = gen.fill(dtype, (B, H, L, d), 6, 0, 0.1)
+    k = gen.fill(dtype, (B, H, L, d), 6, 1, 0.1)
+    v = gen.fill(dtype, (B, H, L, d), 6, 2)
+    jstar = 200
+    # make key j* align with every query strongly: k_j* = 40 * sum of |q| direction
+    qf = gen.to_float64(q, dtype)[0, 0]
+    kstar = 40.0 * np.sign(qf.mean(axis=0) + 1e-9)
+    kk = gen.to_float64(k, dtype)
+    kk[0, 0, jstar] = kstar
+    k = gen.from_float64(kk, dtype)
+    o, _ = run_gpu(q, k, v, dtype, 1.0, 0)
+    s = qf @ gen.to_float64(k, dtype)[0, 0].T
+    others = np.delete(s, jstar, axis=1).max(axis=1)
+    sel = np.where(s[:, jstar] - others >= 60.0)[0]
+    assert sel.size > 0
+    vstar = gen.to_float64(v, dtype)[0, 0, jstar]
+    assert np.max(np.abs(o[0, 0, sel] - vstar)) <= 1e-2
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.F16, gen.F32])
+def test_causal_first_row_is_first_value_row(dtype):
+    B, H, L, d = 1, 2, 333, 128
+    say(f"[closed] causal row 0 dtype={gen.DTYPE_NAMES[dtype]}")
+    q = gen.fill(dtype, (B, H, L, d), 8, 0)
+    k = gen.fill(dtype, (B, H, L, d), 8, 1)
+    v = gen.fill(dtype, (B, H, L, d), 8, 2)
+    o, lse = run_gpu(q, k, v, dtype, 0.125, 1)
+    # one visible key: P = 1 exactly, so O_0 = V_0 bit for bit after rounding
+    np.testing.assert_array_equal(o[:, :, 0], gen.to_float64(v, dtype)[:, :, 0])
+    qk = 0.125 * np.sum(gen.to_float64(q, dtype)[:, :, 0] * gen.to_float64(k, dtype)[:, :, 0], axis=-1)
+    np.testing.assert_allclose(lse[:, :, 0], qk, atol=1e-4)
+
+
+# ---- determinism and no stale tiles ---------------------------------------------
+
+def test_repeat_launch_is_bitwise_identical():
+    import torch
+    cfg = gen.config(1)
+    say("[determinism] workload 1 twice")
+    q, k, v = gen.make_qkv(cfg)
+    o1, l1 = run_gpu(q, k, v, cfg.dtype, cfg.scale, cfg.causal, torch_out=True)
+    o2, l2 = run_gpu(q, k, v, cfg.dtype, cfg.scale, cfg.causal, torch_out=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_outputs_fully_overwritten():
+    """O and lse are written everywhere, whatever they held before."""
+    import torch
+    import io_aware_tiled_02_amd as fa
+    B, H, L, d, dtype = 1, 2, 200, 64, gen.F16
+    say("[overwrite] prefilled outputs")
+    q, k, v = (to_device(gen.fill(dtype, (B, H, L, d), 9, s), dtype) for s in range(3))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, L), float("nan"), device="cuda")
+    fa.forward(q, k, v, 0.125, False, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_forward_on_side_stream():
+    import torch
+    import io_aware_tiled_02_amd as fa
+    B, H, L, d, dtype = 1, 4, 256, 128, gen.BF16
+    say("[stream] side stream")
+    qn, kn, vn = (gen.fill(dtype, (B, H, L, d), 10, s) for s in range(3))
+    q, k, v = (to_device(x, dtype) for x in (qn, kn, vn))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = fa.forward(q, k, v, 0.1, True, stream=s)
+    s.synchronize()
+    o_ref, lse_ref = oracle.fwd(qn, kn, vn, dtype, 0.1, 1)
+    from parity_util import to_host64
+    compare(to_host64(o, dtype), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, dtype, "stream")
