@@ -160,20 +160,15 @@ struct Cfg {
 
 __device__ inline int vswz(int row, int mask) { return (row ^ (row >> 3)) & mask; }
 
-template <class T, int D, bool CAUSAL, int NQB, int NW, int NKB>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(NQB == 1 ? 2 : 1, NQB == 1 ? 2 : 1)))
-void fa_fwd_kernel(Params p) {
-    using C = Cfg<T, D, CAUSAL, NQB, NW, NKB>;
-    using frag = typename Ty<T>::frag;
-    constexpr int E = C::E;
-    constexpr int BC = C::BC;
-
-    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
-
-    // ---- which (head, query tile) this workgroup owns ----
+// Which (batch*head, query tile) workgroup blockIdx.x owns.  Dispatch deals
+// workgroups round-robin to the 8 XCDs (id % 8); when B*H is a multiple of 8
+// the ids are renumbered so that XCD x gets the heads [x*BH/8, (x+1)*BH/8) and
+// therefore all of their query tiles, which share K/V through that XCD's L2.
+// Non-causal: a head's tiles are consecutive in dispatch order.  Causal: the
+// tiles with the most K/V blocks (the last query tiles) are dispatched first.
+template <bool CAUSAL>
+__device__ inline void work_tile(const Params& p, int& bh, int& qt) {
     const int w = blockIdx.x;
-    int bh, qt;
     if (p.remap) {
         const int xcd = w & 7, s = w >> 3, hp = p.BH >> 3;
         if (CAUSAL) {
@@ -190,6 +185,21 @@ void fa_fwd_kernel(Params p) {
         bh = w / p.Tr;
         qt = w % p.Tr;
     }
+}
+
+template <class T, int D, bool CAUSAL, int NQB, int NW, int NKB>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+__attribute__((amdgpu_waves_per_eu(NQB == 1 ? 2 : 1, NQB == 1 ? 2 : 1)))
+void fa_fwd_f32_kernel(Params p) {
+    using C = Cfg<T, D, CAUSAL, NQB, NW, NKB>;
+    using frag = typename Ty<T>::frag;
+    constexpr int E = C::E;
+    constexpr int BC = C::BC;
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+
+    int bh, qt;
+    work_tile<CAUSAL>(p, bh, qt);
 
     const int L = p.L;
     const int tid = threadIdx.x;
@@ -458,6 +468,266 @@ void fa_fwd_kernel(Params p) {
     }
 }
 
+// ===========================================================================
+// 16-bit inputs (bf16, fp16)
+//
+// Same per-wave arithmetic as above, with the K/V staging reworked for gfx950:
+//  * K and V tiles go HBM -> LDS with buffer_load_dwordx4 ... lds (no register
+//    staging, no ds_write).  The buffer descriptor spans exactly one head, so
+//    rows past L read as zeros.
+//  * V stays row-major in LDS; the A operand of O^T += V^T P^T is read with
+//    ds_read_b64_tr_b16, which hands each lane 4 keys of one d column.  In a
+//    16-lane group, lane i receives element i%4 of the 8 bytes addressed by
+//    lane 4e+i/4 as its element e; so lane 16g+4e+q addresses key row e of its
+//    4-key group, d columns 4q..4q+3 of its 16-column band.
+//  * 16-byte chunks are XOR-swizzled per row (K: 16 consecutive rows hit 16
+//    different bank slots with one chunk index; V: 4 consecutive rows spread a
+//    64-byte column band over all slots).  The DMA writes 1 KB per wave
+//    instruction contiguously, so each lane fetches the global chunk that
+//    belongs at its LDS slot.
+//  * Every per-lane LDS offset is computed once; the loop adds only
+//    immediates.
+// ===========================================================================
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+template <int D>
+struct HLayout {
+    static constexpr int P = D * 2;       // row pitch in LDS (bytes), unpadded
+    static constexpr int CPR = D / 8;     // 16-byte chunks per row
+    __device__ static inline int fk(int r) { return (CPR == 16 ? r : (r >> 1)) & (CPR - 1); }
+    __device__ static inline int fv(int r) { return 4 * ((CPR == 16 ? r : (r >> 1)) & (CPR / 4 - 1)); }
+};
+
+// buffer descriptor word 3 for CDNA: raw, untyped 32-bit access
+constexpr int kBufWord3 = 0x00020000;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over [base, base + bytes): reads past the end return 0.
+__device__ inline i32x4 buffer_rsrc(const void* base, int bytes) {
+    const unsigned long long b = (unsigned long long)base;
+    i32x4 r;
+    r[0] = (int)(b & 0xffffffffu);
+    r[1] = (int)(b >> 32);   // stride 0
+    r[2] = bytes;
+    r[3] = kBufWord3;
+    return r;
+}
+
+// 16 bytes per lane from buffer offset `voff` into LDS at lds_base + 16*lane
+// (buffer_load_dwordx4 ... lds).  Issued as inline asm so that the compiler's
+// wait-count insertion does not make later LDS reads wait for this DMA: the
+// kernel waits for it explicitly (vmcnt) before the barrier that publishes the
+// tile.  M0 carries the LDS address and is restored afterwards.
+__device__ inline void dma16(i32x4 rsrc, int voff, unsigned lds_base) {
+    int saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(voff), "s"(rsrc)
+        : "memory");
+}
+
+template <class T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_h_kernel(Params p) {
+    constexpr int NW = 4, QPW = 32, BR = NW * QPW, NKB = 2, BC = 32 * NKB;
+    using Lay = HLayout<D>;
+    constexpr int P = Lay::P;
+    constexpr int TILE = BC * P;          // bytes of one K (or V) tile
+    constexpr int STAGE = 2 * TILE;       // K tile then V tile
+    constexpr int LPW = TILE / 1024 / NW; // 1 KB DMA instructions per wave per tile
+    static_assert(LPW * NW * 1024 == TILE, "tile must split into 1 KB pieces per wave");
+    using frag = typename Ty<T>::frag;
+
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+    int bh, qt;
+    work_tile<CAUSAL>(p, bh, qt);
+
+    const int L = p.L;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hf = lane >> 5;
+    const long long head = (long long)bh * L * D;
+    const char* qh = p.q + head * 2;
+    const i32x4 krs = buffer_rsrc(p.k + head * 2, L * P);
+    const i32x4 vrs = buffer_rsrc(p.v + head * 2, L * P);
+
+    const int q0 = qt * BR;
+    const int qw = q0 + wave * QPW;
+    const int qend = min(q0 + BR, L);
+    const int ntiles = CAUSAL ? (qend + BC - 1) / BC : (L + BC - 1) / BC;
+
+    // Q fragments (B operand of S^T = K Q^T)
+    frag qf[D / 16];
+    {
+        const int row = qw + l32;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            u32x4 raw = u32x4{0, 0, 0, 0};
+            if (row < L) raw = ld16(qh + ((long long)row * D + 16 * s + 8 * hf) * 2);
+            qf[s] = __builtin_bit_cast(frag, raw);
+        }
+        // take the Q loads' wait here, once, instead of at the first use
+        // inside the K/V loop (where it would be repeated every iteration)
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(qf[s]));
+    }
+
+    // DMA mapping: lane byte o = 1024*n + 16*lane of the tile holds row o/P,
+    // slot (o%P)/16, i.e. global chunk slot ^ f(row)
+    int kdma[LPW], vdma[LPW];
+#pragma unroll
+    for (int x = 0; x < LPW; ++x) {
+        const int o = 1024 * (wave * LPW + x) + 16 * lane;
+        const int r = o / P, slot = (o % P) >> 4;
+        kdma[x] = r * P + ((slot ^ Lay::fk(r)) << 4);
+        vdma[x] = r * P + ((slot ^ Lay::fv(r)) << 4);
+    }
+    const unsigned lds0 = (unsigned)(unsigned long long)(lds_char*)smem;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    auto issue = [&](int j, int stage) {
+        const int base = j * TILE;        // byte offset of the tile's first row in the head
+        const unsigned ks = lds0 + stage * STAGE;
+#pragma unroll
+        for (int x = 0; x < LPW; ++x) {
+            const unsigned n = wave_s * LPW + x;
+            dma16(krs, kdma[x] + base, ks + 1024 * n);
+            dma16(vrs, vdma[x] + base, ks + TILE + 1024 * n);
+        }
+    };
+
+    // per-lane LDS read offsets
+    int koff[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) koff[s] = l32 * P + (((2 * s + hf) ^ Lay::fk(l32)) << 4);
+    int voff[D / 32];
+    {
+        const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+        const int rrel = 4 * (g >> 1) + e;            // key row within an 8-key group
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int c = 4 * dt + 2 * (g & 1) + (q >> 1);
+            voff[dt] = rrel * P + ((c ^ Lay::fv(rrel)) << 4) + 8 * (q & 1);
+        }
+    }
+
+    float m_raw = -INFINITY, mc = -INFINITY, lsum = 0.f;
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+
+    issue(0, 0);
+    for (int j = 0; j < ntiles; ++j) {
+        // this thread's DMA for tile j has landed; after the barrier everyone's
+        // has, and every wave is done with tile j-1 (whose stage tile j+1 reuses)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (j + 1 < ntiles) issue(j + 1, (j + 1) & 1);
+
+        const char* ks = smem + (j & 1) * STAGE;
+        const lds_char* vs = (const lds_char*)smem + (j & 1) * STAGE + TILE;
+        const int kb = j * BC;
+        const bool active = !CAUSAL || kb <= qw + QPW - 1;
+        const bool need_mask = (kb + BC > L) || (CAUSAL && kb + BC - 1 > qw);
+        if (!active) continue;
+
+        // S^T = K_j Q^T
+        f32x16 sacc[NKB];
+#pragma unroll
+        for (int kt = 0; kt < NKB; ++kt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+            frag kf[D / 16];
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) kf[s] = __builtin_bit_cast(frag, ld16(ks + kt * 32 * P + koff[s]));
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) sacc[kt] = Ty<T>::mma(kf[s], qf[s], sacc[kt]);
+        }
+
+        if (need_mask) {
+            const int query = qw + l32;
+#pragma unroll
+            for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+                    if (key >= L || (CAUSAL && key > query)) sacc[kt][r] = -INFINITY;
+                }
+        }
+
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_raw, mx);
+        const float ref = (m_new == -INFINITY) ? 0.f : m_new * p.c;
+        const float alpha = __builtin_amdgcn_exp2f(mc - ref);
+        m_raw = m_new;
+        mc = ref;
+        lsum *= alpha;
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        }
+
+        // O^T += V_j^T P^T, one 8-key slice of P at a time
+#pragma unroll
+        for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+            for (int ps = 0; ps < 2; ++ps) {
+                float pe[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * ps + e], p.c, -ref));
+                    lsum += pe[e];
+                }
+                const frag pb = Ty<T>::cvt(pe);
+                const int rowb = (kt * 32 + 16 * ps) * P;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + voff[dt]));
+                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + 8 * P + voff[dt]));
+                    const frag a = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[dt] = Ty<T>::mma(a, pb, oacc[dt]);
+                }
+            }
+    }
+
+    // epilogue: one division by l, logsumexp, stores
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float inv = 1.f / ltot;
+    const int query = qw + l32;
+    if (query < L) {
+        char* orow = p.o + (head + (long long)query * D) * 2;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                T o4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[dt][4 * g + e] * inv);
+                st8(orow + (dt * 32 + g * 8 + hf * 4) * 2, __builtin_bit_cast(u32x2, o4));
+            }
+        if (hf == 0) p.lse[(long long)bh * L + query] = (mc + __builtin_amdgcn_logf(ltot)) * kLn2;
+    }
+}
+
 // ---- host side ----
 
 thread_local int g_last_hip = 0;
@@ -466,35 +736,24 @@ struct Tiling {
     int br, bc;
 };
 
-template <class T, int D, bool CAUSAL>
-struct Choice;
-// bf16 / fp16: 4 waves x 32 rows, 64-key tiles
-template <int D, bool CAUSAL>
-struct Choice<__bf16, D, CAUSAL> {
-    static constexpr int NQB = 1, NW = 4, NKB = 2;
-};
-template <int D, bool CAUSAL>
-struct Choice<_Float16, D, CAUSAL> {
-    static constexpr int NQB = 1, NW = 4, NKB = 2;
-};
-// fp32: 64-key tiles at d = 64, 32-key tiles at d = 128 (LDS budget)
-template <int D, bool CAUSAL>
-struct Choice<float, D, CAUSAL> {
+// Tile shapes: 16-bit types use fa_fwd_h_kernel (4 waves x 32 query rows,
+// 64-key tiles); fp32 uses fa_fwd_f32_kernel (64-key tiles at d = 64, 32-key
+// tiles at d = 128 for the LDS budget).
+template <class T, int D>
+struct F32Choice {
     static constexpr int NQB = 1, NW = 4, NKB = (D == 64 ? 2 : 1);
+    using C = Cfg<float, D, false, NQB, NW, NKB>;
 };
 
 template <class T, int D, bool CAUSAL>
 Tiling tiling_of() {
-    using Ch = Choice<T, D, CAUSAL>;
-    using C = Cfg<T, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>;
+    if constexpr (sizeof(T) == 2) return Tiling{128, 64};
+    using C = typename F32Choice<T, D>::C;
     return Tiling{C::BR, C::BC};
 }
 
-template <class T, int D, bool CAUSAL>
-int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int L, float scale,
-           hipStream_t stream) {
-    using Ch = Choice<T, D, CAUSAL>;
-    using C = Cfg<T, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>;
+inline Params make_params(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int L,
+                          float scale, int br) {
     Params p;
     p.q = static_cast<const char*>(q);
     p.k = static_cast<const char*>(k);
@@ -503,19 +762,36 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     p.lse = lse;
     p.L = L;
     p.BH = BH;
-    p.Tr = (L + C::BR - 1) / C::BR;
+    p.Tr = (L + br - 1) / br;
     p.remap = (BH % 8 == 0) ? 1 : 0;
     p.c = scale * kLog2e;
     p.scale = scale;
-    const long long grid = (long long)BH * p.Tr;
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>), dim3((unsigned)grid),
-                       dim3(C::NT), 0, stream, p);
+    return p;
+}
+
+inline int launch_status() {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) {
         g_last_hip = (int)err;
         return FA_ERR_HIP;
     }
     return FA_OK;
+}
+
+template <class T, int D, bool CAUSAL>
+int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int L, float scale,
+           hipStream_t stream) {
+    const Tiling t = tiling_of<T, D, CAUSAL>();
+    const Params p = make_params(q, k, v, o, lse, BH, L, scale, t.br);
+    const long long grid = (long long)BH * p.Tr;
+    if constexpr (sizeof(T) == 2) {
+        hipLaunchKernelGGL((fa_fwd_h_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    } else {
+        using Ch = F32Choice<T, D>;
+        hipLaunchKernelGGL((fa_fwd_f32_kernel<float, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>), dim3((unsigned)grid),
+                           dim3(Ch::C::NT), 0, stream, p);
+    }
+    return launch_status();
 }
 
 template <class T>
@@ -537,6 +813,8 @@ int check_args(int B, int H, int L, int d, int causal, int dtype) {
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     const long long n = (long long)B * H * L;
     if (n >= (1LL << 62) / d) return FA_ERR_INVALID_ARG;
+    // one head's tensor must stay below 2 GiB (32-bit buffer byte offsets)
+    if ((long long)L * d * (dtype == FA_F32 ? 4 : 2) >= (1LL << 31)) return FA_ERR_INVALID_ARG;
     const Tiling t = tiling_dispatch(d, causal, dtype);
     const long long grid = (long long)B * H * ((L + t.br - 1) / t.br);
     if (grid > 0x7fffffffLL || (long long)B * H > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
