@@ -42,6 +42,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa.h"
 
 namespace {
@@ -534,26 +536,66 @@ __device__ inline void dma16(i32x4 rsrc, int voff, unsigned lds_base) {
         : "memory");
 }
 
+// Exchange with lane^32 (v_permlane32_swap): returns the pair {x, x of lane^32}.
+__device__ inline float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+#ifndef FA_H_NKB128
+#define FA_H_NKB128 4
+#endif
+#ifndef FA_H_NKB64
+#define FA_H_NKB64 4
+#endif
+
+// Tile shape of the 16-bit kernel: 8 waves x 32 query rows, 32*NKB-key tiles.
+template <int D>
+struct HCfg {
+    static constexpr int NW = 8, QPW = 32, BR = NW * QPW, NKB = (D == 128 ? FA_H_NKB128 : FA_H_NKB64), BC = 32 * NKB;
+    static constexpr int P = D * 2;                 // LDS row pitch (bytes)
+    static constexpr int TILE = BC * P;             // one K or V tile (bytes)
+    static constexpr int LPW = TILE / 1024 / NW;    // 1 KB DMA instructions per wave per tile
+    static_assert(LPW >= 1 && LPW * NW * 1024 == TILE, "tile must split into 1 KB pieces per wave");
+    // LDS: K stage 0, K stage 1, V stage 0, V stage 1
+    static constexpr int BYTES = 4 * TILE;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Ping-pong schedule.  The 8 waves form two groups of 4 (waves 0-3 and 4-7);
+// each SIMD runs one wave of each group.  Per K/V tile j a wave has
+//     M(j): O^T += V_{j-1}^T P_{j-1}^T  and  S_j = K_j Q^T        (MFMA)
+//     X(j): row max, rescale, P_j = exp2(scale*S_j - ref), l     (VALU)
+// and the groups run them in alternate phases fenced by workgroup barriers:
+//     phase   0    1    2    3   ...  2T   2T+1
+//     group 0 M(0) X(0) M(1) X(1) ... M(T)  -
+//     group 1  -   M(0) X(0) M(1) ... X(T-1) M(T)
+// so while one wave of a SIMD feeds the matrix core the other keeps the VALU
+// busy with the softmax.  M(T) only finishes the last PV.  K_j and V_{j-1}
+// are read in phases 2j and 2j+1; the DMA for K_{j+1} and V_j is issued at
+// the start of phase 2j into the other stages and waited for at its end.
 template <class T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_h_kernel(Params p) {
-    constexpr int NW = 4, QPW = 32, BR = NW * QPW, NKB = 2, BC = 32 * NKB;
+    using Cf = HCfg<D>;
+    constexpr int QPW = Cf::QPW, BR = Cf::BR, NKB = Cf::NKB, BC = Cf::BC;
+    constexpr int P = Cf::P, TILE = Cf::TILE, LPW = Cf::LPW;
     using Lay = HLayout<D>;
-    constexpr int P = Lay::P;
-    constexpr int TILE = BC * P;          // bytes of one K (or V) tile
-    constexpr int STAGE = 2 * TILE;       // K tile then V tile
-    constexpr int LPW = TILE / 1024 / NW; // 1 KB DMA instructions per wave per tile
-    static_assert(LPW * NW * 1024 == TILE, "tile must split into 1 KB pieces per wave");
     using frag = typename Ty<T>::frag;
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[Cf::BYTES];
 
     int bh, qt;
     work_tile<CAUSAL>(p, bh, qt);
 
     const int L = p.L;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int group = wave >> 2;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hf = lane >> 5;
@@ -563,9 +605,11 @@ void fa_fwd_h_kernel(Params p) {
     const i32x4 vrs = buffer_rsrc(p.v + head * 2, L * P);
 
     const int q0 = qt * BR;
-    const int qw = q0 + wave * QPW;
+    const int qw = q0 + wave * QPW;                 // this wave's first query row
     const int qend = min(q0 + BR, L);
-    const int ntiles = CAUSAL ? (qend + BC - 1) / BC : (L + BC - 1) / BC;
+    const int ntiles = CAUSAL ? (qend + BC - 1) / BC : (L + BC - 1) / BC;   // K/V tiles of the workgroup
+    // K/V tiles this wave computes (0 for a wave entirely past L)
+    const int ntw = qw >= L ? 0 : (CAUSAL ? (min(qw + QPW, L) + BC - 1) / BC : ntiles);
 
     // Q fragments (B operand of S^T = K Q^T)
     frag qf[D / 16];
@@ -577,35 +621,44 @@ void fa_fwd_h_kernel(Params p) {
             if (row < L) raw = ld16(qh + ((long long)row * D + 16 * s + 8 * hf) * 2);
             qf[s] = __builtin_bit_cast(frag, raw);
         }
-        // take the Q loads' wait here, once, instead of at the first use
-        // inside the K/V loop (where it would be repeated every iteration)
+        // take the Q loads' wait here, once, instead of inside the K/V loop
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(qf[s]));
     }
 
-    // DMA mapping: lane byte o = 1024*n + 16*lane of the tile holds row o/P,
-    // slot (o%P)/16, i.e. global chunk slot ^ f(row)
-    int kdma[LPW], vdma[LPW];
+    // DMA mapping: byte o = 1024*n + 16*lane of a tile holds row o/P, slot
+    // (o%P)/16, i.e. global chunk slot ^ f(row) of that row
+    int kdma[LPW], vdma[LPW], kdma2[LPW], vdma2[LPW];
 #pragma unroll
     for (int x = 0; x < LPW; ++x) {
         const int o = 1024 * (wave * LPW + x) + 16 * lane;
         const int r = o / P, slot = (o % P) >> 4;
         kdma[x] = r * P + ((slot ^ Lay::fk(r)) << 4);
         vdma[x] = r * P + ((slot ^ Lay::fv(r)) << 4);
+        const int o2 = o + 4096 * LPW;           // the same lane's piece for wave + 4
+        const int r2 = o2 / P, slot2 = (o2 % P) >> 4;
+        kdma2[x] = r2 * P + ((slot2 ^ Lay::fk(r2)) << 4);
+        vdma2[x] = r2 * P + ((slot2 ^ Lay::fv(r2)) << 4);
     }
     const unsigned lds0 = (unsigned)(unsigned long long)(lds_char*)smem;
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    auto issue = [&](int j, int stage) {
-        const int base = j * TILE;        // byte offset of the tile's first row in the head
-        const unsigned ks = lds0 + stage * STAGE;
+    // the lead group (waves 0-3) issues the whole tile: its own share and that
+    // of wave+4
+    auto issue_k2 = [&](int j) {
+        const unsigned dst = lds0 + (j & 1) * TILE + 1024 * wave * LPW;
 #pragma unroll
         for (int x = 0; x < LPW; ++x) {
-            const unsigned n = wave_s * LPW + x;
-            dma16(krs, kdma[x] + base, ks + 1024 * n);
-            dma16(vrs, vdma[x] + base, ks + TILE + 1024 * n);
+            dma16(krs, kdma[x] + j * TILE, __builtin_amdgcn_readfirstlane(dst + 1024 * x));
+            dma16(krs, kdma2[x] + j * TILE, __builtin_amdgcn_readfirstlane(dst + 4096 * LPW + 1024 * x));
         }
     };
-
+    auto issue_v2 = [&](int j) {
+        const unsigned dst = lds0 + 2 * TILE + (j & 1) * TILE + 1024 * wave * LPW;
+#pragma unroll
+        for (int x = 0; x < LPW; ++x) {
+            dma16(vrs, vdma[x] + j * TILE, __builtin_amdgcn_readfirstlane(dst + 1024 * x));
+            dma16(vrs, vdma2[x] + j * TILE, __builtin_amdgcn_readfirstlane(dst + 4096 * LPW + 1024 * x));
+        }
+    };
     // per-lane LDS read offsets
     int koff[D / 16];
 #pragma unroll
@@ -627,53 +680,89 @@ void fa_fwd_h_kernel(Params p) {
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+    f32x16 sacc[NKB];
+    frag pf[NKB][2];            // P of the last softmax phase, as MFMA B operands
 
-    issue(0, 0);
-    for (int j = 0; j < ntiles; ++j) {
-        // this thread's DMA for tile j has landed; after the barrier everyone's
-        // has, and every wave is done with tile j-1 (whose stage tile j+1 reuses)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (j + 1 < ntiles) issue(j + 1, (j + 1) & 1);
-
-        const char* ks = smem + (j & 1) * STAGE;
-        const lds_char* vs = (const lds_char*)smem + (j & 1) * STAGE + TILE;
-        const int kb = j * BC;
-        const bool active = !CAUSAL || kb <= qw + QPW - 1;
-        const bool need_mask = (kb + BC > L) || (CAUSAL && kb + BC - 1 > qw);
-        if (!active) continue;
-
-        // S^T = K_j Q^T
-        f32x16 sacc[NKB];
+    // M(j): PV of tile j-1, scores of tile j.  The MFMAs run in slices of
+    // up to 4 (PV: one 8-key slice of P against the D/32 tiles of V^T;
+    // scores: 4 d-steps of one 32-key sub-tile); the operands of slice i+1 are
+    // read from LDS while slice i runs, and scheduling barriers keep the
+    // compiler from hoisting further reads (register budget).
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    auto mma_run = [&](auto pv_tag, auto s_tag, int j) {
+        constexpr bool PV = decltype(pv_tag)::value;
+        constexpr bool SC = decltype(s_tag)::value;
+        constexpr int GPT = D / 64;                       // score slices per 32-key sub-tile
+        constexpr int NPV = PV ? 2 * NKB : 0;
+        constexpr int NSL = NPV + (SC ? NKB * GPT : 0);
+        const lds_char* vs = (const lds_char*)smem + 2 * TILE + ((j - 1) & 1) * TILE;
+        const char* ks = smem + (j & 1) * TILE;
+        frag buf[2][4];
+        auto load = [&](int i) {
+            if (i < NPV) {
+                const int rowb = ((i >> 1) * 32 + 16 * (i & 1)) * P;
 #pragma unroll
-        for (int kt = 0; kt < NKB; ++kt) {
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + voff[dt]));
+                    const v4i16 hi =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + 8 * P + voff[dt]));
+                    buf[i & 1][dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+            } else {
+                const int g = i - NPV, kt = g / GPT, s0 = 4 * (g % GPT);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-            frag kf[D / 16];
+                for (int x = 0; x < 4; ++x)
+                    buf[i & 1][x] = __builtin_bit_cast(frag, ld16(ks + kt * 32 * P + koff[s0 + x]));
+            }
+        };
+        auto exec = [&](int i) {
+            if (i < NPV) {
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) kf[s] = __builtin_bit_cast(frag, ld16(ks + kt * 32 * P + koff[s]));
+                for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = Ty<T>::mma(buf[i & 1][dt], pf[i >> 1][i & 1], oacc[dt]);
+            } else {
+                const int g = i - NPV, kt = g / GPT, s0 = 4 * (g % GPT);
+                if (s0 == 0) {
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) sacc[kt] = Ty<T>::mma(kf[s], qf[s], sacc[kt]);
+                    for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+                }
+#pragma unroll
+                for (int x = 0; x < 4; ++x) sacc[kt] = Ty<T>::mma(buf[i & 1][x], qf[s0 + x], sacc[kt]);
+            }
+        };
+        load(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) {
+            if (i + 1 < NSL) load(i + 1);
+            exec(i);
+            __builtin_amdgcn_sched_barrier(0);
         }
-
-        if (need_mask) {
-            const int query = qw + l32;
+    };
+    // X(j): online-softmax update for tile j (MASK: the tile reaches past L
+    // or past this wave's first query); leaves P_j in pf
+    auto softmax_run = [&](auto mask_tag, int j) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int kb = j * BC;
+        if constexpr (MASK) {
+            // register r of sub-tile kt holds key kb + 4*hf + c with the
+            // constant c = 32*kt + 8*(r/4) + r%4; the key is masked when it is
+            // past the query (causal) or past L-1, i.e. when c > lim
+            const int last = CAUSAL ? min(qw + l32, L - 1) : L - 1;
+            const int lim = last - kb - 4 * hf;
 #pragma unroll
             for (int kt = 0; kt < NKB; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb + kt * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-                    if (key >= L || (CAUSAL && key > query)) sacc[kt][r] = -INFINITY;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kt + 8 * (r >> 2) + (r & 3) > lim) sacc[kt][r] = -INFINITY;
         }
-
         float mx = sacc[0][0];
 #pragma unroll
         for (int kt = 0; kt < NKB; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_raw, mx);
+        const float m_new = fmaxf(m_raw, pair_max(mx));
+        // exponent reference: scale*m_new in log2 units (0 while no key is seen)
         const float ref = (m_new == -INFINITY) ? 0.f : m_new * p.c;
         const float alpha = __builtin_amdgcn_exp2f(mc - ref);
         m_raw = m_new;
@@ -685,8 +774,6 @@ void fa_fwd_h_kernel(Params p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
         }
-
-        // O^T += V_j^T P^T, one 8-key slice of P at a time
 #pragma unroll
         for (int kt = 0; kt < NKB; ++kt)
 #pragma unroll
@@ -697,20 +784,88 @@ void fa_fwd_h_kernel(Params p) {
                     pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * ps + e], p.c, -ref));
                     lsum += pe[e];
                 }
-                const frag pb = Ty<T>::cvt(pe);
-                const int rowb = (kt * 32 + 16 * ps) * P;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + voff[dt]));
-                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + 8 * P + voff[dt]));
-                    const frag a = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[dt] = Ty<T>::mma(a, pb, oacc[dt]);
-                }
+                pf[kt][ps] = Ty<T>::cvt(pe);
             }
+    };
+
+    // Group 0 issues every DMA (tile j's at the start of its M(j) slot) and
+    // waits for it at the end of its X(j) slot; group 1 runs one phase behind.
+    const bool lead = group == 0;
+    auto dma_tile = [&](int j) {                  // K_{j+1}, V_j
+        if (lead) {
+            if (j + 1 < ntiles) issue_k2(j + 1);
+            issue_v2(j);
+        }
+    };
+    // The softmax phase's results are consumed only in the next MFMA phase, so
+    // the compiler would sink the exp / convert / sum work past the barrier
+    // into it.  An empty asm that "modifies" them pins that work here.
+    auto pin_x = [&]() {
+#pragma unroll
+        for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+            for (int ps = 0; ps < 2; ++ps) asm volatile("" : "+v"(pf[kt][ps]));
+        asm volatile("" : "+v"(lsum), "+v"(mc), "+v"(m_raw));
+    };
+    // phase boundaries: the scheduling barriers keep the compiler from
+    // moving register-only work (row max, MFMAs) across the workgroup barrier,
+    // which would undo the phase split
+    auto end_m = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto end_x = [&]() {
+        pin_x();
+        __builtin_amdgcn_sched_barrier(0);
+        if (lead) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // first tile whose keys can reach past L or past this wave's first query
+    const int jmask = CAUSAL ? min(qw / BC, (L - 1) / BC) : (L - 1) / BC;
+
+    if (lead) issue_k2(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (!lead) __syncthreads();                   // group 1 starts one phase later
+    int j = 0;
+    if (ntw > 0) {
+        dma_tile(0);
+        mma_run(no{}, yes{}, 0);
+        end_m();
+        if (jmask == 0) softmax_run(yes{}, 0);
+        else softmax_run(no{}, 0);
+        end_x();
+        for (j = 1; j < min(jmask, ntw); ++j) {   // steady state, no masking
+            dma_tile(j);
+            mma_run(yes{}, yes{}, j);
+            end_m();
+            softmax_run(no{}, j);
+            end_x();
+        }
+        for (j = max(j, 1); j < ntw; ++j) {      // tiles that need the mask
+            dma_tile(j);
+            mma_run(yes{}, yes{}, j);
+            end_m();
+            softmax_run(yes{}, j);
+            end_x();
+        }
+        if (j < ntiles) dma_tile(j);              // j == ntw: last PV
+        mma_run(yes{}, no{}, j);
+        end_m();
+        if (j < ntiles) end_x();
+        ++j;
     }
+    for (; j <= ntiles; ++j) {                    // phases of tiles this wave does not need
+        if (j < ntiles) dma_tile(j);
+        end_m();
+        if (j < ntiles) end_x();
+    }
+    if (lead) __syncthreads();                    // group 0 ends one phase later
 
     // epilogue: one division by l, logsumexp, stores
-    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float ltot = pair_sum(lsum);
     const float inv = 1.f / ltot;
     const int query = qw + l32;
     if (query < L) {
@@ -747,7 +902,7 @@ struct F32Choice {
 
 template <class T, int D, bool CAUSAL>
 Tiling tiling_of() {
-    if constexpr (sizeof(T) == 2) return Tiling{128, 64};
+    if constexpr (sizeof(T) == 2) return Tiling{HCfg<D>::BR, HCfg<D>::BC};
     using C = typename F32Choice<T, D>::C;
     return Tiling{C::BR, C::BC};
 }
@@ -785,7 +940,7 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     const Params p = make_params(q, k, v, o, lse, BH, L, scale, t.br);
     const long long grid = (long long)BH * p.Tr;
     if constexpr (sizeof(T) == 2) {
-        hipLaunchKernelGGL((fa_fwd_h_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((fa_fwd_h_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(HCfg<D>::NW * 64), 0, stream, p);
     } else {
         using Ch = F32Choice<T, D>;
         hipLaunchKernelGGL((fa_fwd_f32_kernel<float, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>), dim3((unsigned)grid),
