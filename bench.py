@@ -57,7 +57,7 @@ def cpu_baseline(cfg, q, k, v, target_s: float):
     import oracle
     nth = oracle.max_threads()
     per_row = 4.0 * cfg.L * cfg.d * (0.5 if cfg.causal else 1.0)   # metric FLOPs of one query row
-    rows0 = gen.sample_rows(cfg.L, min(16, cfg.L), cfg.seed)
+    rows0 = gen.sample_rows(cfg.L, min(128, cfg.L), cfg.seed)
     t = time.perf_counter()
     oracle.fwd(q, k, v, cfg.dtype, cfg.scale, cfg.causal, rows0)
     t0 = max(time.perf_counter() - t, 1e-3)
@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="workload index 0..4 (default 3)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -107,6 +109,20 @@ def main():
 
     import torch
     import io_aware_tiled_02_amd as fa
+
+    if args.copy_probe:
+        # A plain copy of known size: FETCH_SIZE / WRITE_SIZE read on it give
+        # the factor between those counters and bytes actually moved.
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return
 
     cfg = gen.config(args.workload)
     log(f"[bench] workload {cfg.index}: {cfg.name}; generating inputs")
@@ -157,7 +173,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": tflops / peak,
         "traffic": traffic,
-        "kernel": "fa_fwd_kernel",
+        "kernel": "fa_fwd_h_kernel" if cfg.dtype != gen.F32 else "fa_fwd_f32_kernel",
         "per_launch_flops": cfg.flops,
         "avg_launch_ms": ms,
         "algorithmic_bytes_per_launch": cfg.algorithmic_bytes,
