@@ -627,11 +627,13 @@ void fa_fwd_h_kernel(Params p) {
     }
 
     // DMA mapping: byte o = 1024*n + 16*lane of a tile holds row o/P, slot
-    // (o%P)/16, i.e. global chunk slot ^ f(row) of that row
+    // (o%P)/16, i.e. global chunk slot ^ f(row) of that row.  One wave of the
+    // issuing group covers the 1 KB pieces n of waves (wave & 3) and (wave & 3) + 4.
+    const int wq = wave & 3;
     int kdma[LPW], vdma[LPW], kdma2[LPW], vdma2[LPW];
 #pragma unroll
     for (int x = 0; x < LPW; ++x) {
-        const int o = 1024 * (wave * LPW + x) + 16 * lane;
+        const int o = 1024 * (wq * LPW + x) + 16 * lane;
         const int r = o / P, slot = (o % P) >> 4;
         kdma[x] = r * P + ((slot ^ Lay::fk(r)) << 4);
         vdma[x] = r * P + ((slot ^ Lay::fv(r)) << 4);
@@ -641,10 +643,8 @@ void fa_fwd_h_kernel(Params p) {
         vdma2[x] = r2 * P + ((slot2 ^ Lay::fv(r2)) << 4);
     }
     const unsigned lds0 = (unsigned)(unsigned long long)(lds_char*)smem;
-    // the lead group (waves 0-3) issues the whole tile: its own share and that
-    // of wave+4
     auto issue_k2 = [&](int j) {
-        const unsigned dst = lds0 + (j & 1) * TILE + 1024 * wave * LPW;
+        const unsigned dst = lds0 + (j & 1) * TILE + 1024 * wq * LPW;
 #pragma unroll
         for (int x = 0; x < LPW; ++x) {
             dma16(krs, kdma[x] + j * TILE, __builtin_amdgcn_readfirstlane(dst + 1024 * x));
@@ -652,7 +652,7 @@ void fa_fwd_h_kernel(Params p) {
         }
     };
     auto issue_v2 = [&](int j) {
-        const unsigned dst = lds0 + 2 * TILE + (j & 1) * TILE + 1024 * wave * LPW;
+        const unsigned dst = lds0 + 2 * TILE + (j & 1) * TILE + 1024 * wq * LPW;
 #pragma unroll
         for (int x = 0; x < LPW; ++x) {
             dma16(vrs, vdma[x] + j * TILE, __builtin_amdgcn_readfirstlane(dst + 1024 * x));
@@ -788,14 +788,18 @@ void fa_fwd_h_kernel(Params p) {
             }
     };
 
-    // Group 0 issues every DMA (tile j's at the start of its M(j) slot) and
-    // waits for it at the end of its X(j) slot; group 1 runs one phase behind.
-    const bool lead = group == 0;
-    auto dma_tile = [&](int j) {                  // K_{j+1}, V_j
-        if (lead) {
-            if (j + 1 < ntiles) issue_k2(j + 1);
-            issue_v2(j);
-        }
+    // Group 1 issues every DMA, in its softmax phases, which leaves the MFMA
+    // phases free of memory-instruction issue: the DMA for K_{t+1} and V_t
+    // goes out at the start of phase 2t (group 1's X(t-1), or its first, idle
+    // phase for t = 0) and is waited for at the end of phase 2t+1 (group 1's
+    // M(t)); the barrier there publishes the stages.
+    const bool feeder = group == 1;
+    auto dma_tile = [&](int t) {                  // K_{t+1}, V_t
+        if (t + 1 < ntiles) issue_k2(t + 1);
+        issue_v2(t);
+    };
+    auto start_x = [&](int j) {                   // start of X(j) = phase 2j+2 (group 1)
+        if (feeder && j + 1 < ntiles) dma_tile(j + 1);
     };
     // The softmax phase's results are consumed only in the next MFMA phase, so
     // the compiler would sink the exp / convert / sum work past the barrier
@@ -812,57 +816,64 @@ void fa_fwd_h_kernel(Params p) {
     // which would undo the phase split
     auto end_m = [&]() {
         __builtin_amdgcn_sched_barrier(0);
+        if (feeder) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
     auto end_x = [&]() {
         pin_x();
         __builtin_amdgcn_sched_barrier(0);
-        if (lead) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
     // first tile whose keys can reach past L or past this wave's first query
     const int jmask = CAUSAL ? min(qw / BC, (L - 1) / BC) : (L - 1) / BC;
 
-    if (lead) issue_k2(0);
+    if (feeder) issue_k2(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (!lead) __syncthreads();                   // group 1 starts one phase later
+    if (feeder) {                                 // group 1's first phase: DMA only
+        dma_tile(0);
+        __syncthreads();
+    }
     int j = 0;
     if (ntw > 0) {
-        dma_tile(0);
         mma_run(no{}, yes{}, 0);
         end_m();
+        start_x(0);
         if (jmask == 0) softmax_run(yes{}, 0);
         else softmax_run(no{}, 0);
         end_x();
         for (j = 1; j < min(jmask, ntw); ++j) {   // steady state, no masking
-            dma_tile(j);
             mma_run(yes{}, yes{}, j);
             end_m();
+            start_x(j);
             softmax_run(no{}, j);
             end_x();
         }
         for (j = max(j, 1); j < ntw; ++j) {      // tiles that need the mask
-            dma_tile(j);
             mma_run(yes{}, yes{}, j);
             end_m();
+            start_x(j);
             softmax_run(yes{}, j);
             end_x();
         }
-        if (j < ntiles) dma_tile(j);              // j == ntw: last PV
-        mma_run(yes{}, no{}, j);
+        mma_run(yes{}, no{}, j);                  // j == ntw: last PV
         end_m();
-        if (j < ntiles) end_x();
+        if (j < ntiles) {
+            start_x(j);
+            end_x();
+        }
         ++j;
     }
     for (; j <= ntiles; ++j) {                    // phases of tiles this wave does not need
-        if (j < ntiles) dma_tile(j);
         end_m();
-        if (j < ntiles) end_x();
+        if (j < ntiles) {
+            start_x(j);
+            end_x();
+        }
     }
-    if (lead) __syncthreads();                    // group 0 ends one phase later
+    if (!feeder) __syncthreads();                 // group 0 ends one phase later
 
     // epilogue: one division by l, logsumexp, stores
     const float ltot = pair_sum(lsum);
