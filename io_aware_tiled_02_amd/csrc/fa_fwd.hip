@@ -566,6 +566,21 @@ struct HCfg {
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
+// Issue order of the MFMA slices of one phase: the NPV slices of P V (whose
+// operands come from transposing LDS reads, the slower kind) are spread
+// evenly among the NS score slices so LDS demand stays level.
+template <int NPV, int NS>
+struct SliceOrder {
+    int v[NPV + NS > 0 ? NPV + NS : 1];
+    constexpr SliceOrder() : v{} {
+        int p = 0, s = 0;
+        for (int i = 0; i < NPV + NS; ++i) {
+            if (s >= NS || (p < NPV && p * NS <= s * NPV)) v[i] = p++;
+            else v[i] = NPV + s++;
+        }
+    }
+};
+
 // Ping-pong schedule.  The 8 waves form two groups of 4 (waves 0-3 and 4-7);
 // each SIMD runs one wave of each group.  Per K/V tile j a wave has
 //     M(j): O^T += V_{j-1}^T P_{j-1}^T  and  S_j = K_j Q^T        (MFMA)
@@ -576,8 +591,8 @@ struct HCfg {
 //     group 1  -   M(0) X(0) M(1) ... X(T-1) M(T)
 // so while one wave of a SIMD feeds the matrix core the other keeps the VALU
 // busy with the softmax.  M(T) only finishes the last PV.  K_j and V_{j-1}
-// are read in phases 2j and 2j+1; the DMA for K_{j+1} and V_j is issued at
-// the start of phase 2j into the other stages and waited for at its end.
+// are read in phases 2j and 2j+1; the DMA for K_{j+1} and V_j goes into the
+// other stages during phase 2j and is complete by the end of phase 2j+1.
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_h_kernel(Params p) {
@@ -628,35 +643,30 @@ void fa_fwd_h_kernel(Params p) {
 
     // DMA mapping: byte o = 1024*n + 16*lane of a tile holds row o/P, slot
     // (o%P)/16, i.e. global chunk slot ^ f(row) of that row.  One wave of the
-    // issuing group covers the 1 KB pieces n of waves (wave & 3) and (wave & 3) + 4.
+    // issuing group covers the 1 KB pieces n = (wave & 3)*LPW + x of wave
+    // (wave & 3) and the same pieces of wave (wave & 3) + 4, 4096*LPW bytes on.
+    // Over x the K offsets differ by 1024*x in the row bits and 4*x in the
+    // swizzled chunk, bits disjoint from the rest (the K swizzle of row
+    // 4x + g is 4x | g at d = 128 and (4x | g) & 7 at d = 64), so piece x is
+    // kd0 ^ (x * 0x440); the V swizzle repeats every 4 rows, so its piece x
+    // is vd0 + 1024*x.
     const int wq = wave & 3;
-    int kdma[LPW], vdma[LPW], kdma2[LPW], vdma2[LPW];
-#pragma unroll
-    for (int x = 0; x < LPW; ++x) {
-        const int o = 1024 * (wq * LPW + x) + 16 * lane;
+    int kd0, vd0;
+    {
+        const int o = 1024 * (wq * LPW) + 16 * lane;
         const int r = o / P, slot = (o % P) >> 4;
-        kdma[x] = r * P + ((slot ^ Lay::fk(r)) << 4);
-        vdma[x] = r * P + ((slot ^ Lay::fv(r)) << 4);
-        const int o2 = o + 4096 * LPW;           // the same lane's piece for wave + 4
-        const int r2 = o2 / P, slot2 = (o2 % P) >> 4;
-        kdma2[x] = r2 * P + ((slot2 ^ Lay::fk(r2)) << 4);
-        vdma2[x] = r2 * P + ((slot2 ^ Lay::fv(r2)) << 4);
+        kd0 = r * P + ((slot ^ Lay::fk(r)) << 4);
+        vd0 = r * P + ((slot ^ Lay::fv(r)) << 4);
     }
+    auto kdma_off = [&](int x, int hi) { return (kd0 ^ (x * 0x440)) + hi * 4096 * LPW; };
+    auto vdma_off = [&](int x, int hi) { return vd0 + 1024 * x + hi * 4096 * LPW; };
     const unsigned lds0 = (unsigned)(unsigned long long)(lds_char*)smem;
     auto issue_k2 = [&](int j) {
         const unsigned dst = lds0 + (j & 1) * TILE + 1024 * wq * LPW;
 #pragma unroll
         for (int x = 0; x < LPW; ++x) {
-            dma16(krs, kdma[x] + j * TILE, __builtin_amdgcn_readfirstlane(dst + 1024 * x));
-            dma16(krs, kdma2[x] + j * TILE, __builtin_amdgcn_readfirstlane(dst + 4096 * LPW + 1024 * x));
-        }
-    };
-    auto issue_v2 = [&](int j) {
-        const unsigned dst = lds0 + 2 * TILE + (j & 1) * TILE + 1024 * wq * LPW;
-#pragma unroll
-        for (int x = 0; x < LPW; ++x) {
-            dma16(vrs, vdma[x] + j * TILE, __builtin_amdgcn_readfirstlane(dst + 1024 * x));
-            dma16(vrs, vdma2[x] + j * TILE, __builtin_amdgcn_readfirstlane(dst + 4096 * LPW + 1024 * x));
+            dma16(krs, kdma_off(x, 0) + j * TILE, __builtin_amdgcn_readfirstlane(dst + 1024 * x));
+            dma16(krs, kdma_off(x, 1) + j * TILE, __builtin_amdgcn_readfirstlane(dst + 4096 * LPW + 1024 * x));
         }
     };
     // per-lane LDS read offsets
@@ -674,7 +684,7 @@ void fa_fwd_h_kernel(Params p) {
         }
     }
 
-    float m_raw = -INFINITY, mc = -INFINITY, lsum = 0.f;
+    float mc = -INFINITY, lsum = 0.f;
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -683,11 +693,44 @@ void fa_fwd_h_kernel(Params p) {
     f32x16 sacc[NKB];
     frag pf[NKB][2];            // P of the last softmax phase, as MFMA B operands
 
+    // Group 0 issues every K/V DMA, from its MFMA phases: in M(t) (phase 2t)
+    // the 1 KB pieces of K_{t+1} and V_t go out one or two after each MFMA
+    // slice, where the wave otherwise waits on the matrix core, and group 0
+    // waits for them at the end of its X(t) (phase 2t+1); the barrier there
+    // publishes the stages, which are first read in phase 2t+2.
+    const bool feeder = group == 0;
+    constexpr int NPIECE = 4 * LPW;               // DMA instructions per wave for K_{t+1}, V_t
+    auto dma_piece = [&](int t, int n) {          // n-th instruction of K_{t+1}, V_t
+        const int x = (n >> 1) % LPW, hi = n & 1;
+        if (n < 2 * LPW) {
+            if (t + 1 < ntiles) {
+                const unsigned dst = lds0 + ((t + 1) & 1) * TILE + 1024 * (wq * LPW + x) + hi * 4096 * LPW;
+                dma16(krs, kdma_off(x, hi) + (t + 1) * TILE, __builtin_amdgcn_readfirstlane(dst));
+            }
+        } else {
+            const unsigned dst = lds0 + 2 * TILE + (t & 1) * TILE + 1024 * (wq * LPW + x) + hi * 4096 * LPW;
+            dma16(vrs, vdma_off(x, hi) + t * TILE, __builtin_amdgcn_readfirstlane(dst));
+        }
+    };
+    auto dma_tile = [&](int t) {                  // all of K_{t+1}, V_t at once (phases without MFMAs)
+#pragma unroll
+        for (int n = 0; n < NPIECE; ++n) dma_piece(t, n);
+    };
+    // after MFMA slice pos of nsl in M(t): its share of the pieces
+    auto mfeed = [&](int t, int pos, int nsl) {
+        if (feeder && t < ntiles) {
+            const int n0 = (pos * NPIECE + nsl - 1) / nsl, n1 = ((pos + 1) * NPIECE + nsl - 1) / nsl;
+#pragma unroll
+            for (int n = n0; n < n1; ++n) dma_piece(t, n);
+        }
+    };
+
     // M(j): PV of tile j-1, scores of tile j.  The MFMAs run in slices of
     // up to 4 (PV: one 8-key slice of P against the D/32 tiles of V^T;
-    // scores: 4 d-steps of one 32-key sub-tile); the operands of slice i+1 are
-    // read from LDS while slice i runs, and scheduling barriers keep the
-    // compiler from hoisting further reads (register budget).
+    // scores: 4 d-steps of one 32-key sub-tile), PV slices spread among the
+    // score slices.  The operands of slice i+1 are read from LDS while
+    // slice i runs: after each MFMA of slice i goes its share of those reads,
+    // so that reads neither queue behind a burst nor land just before use.
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
     auto mma_run = [&](auto pv_tag, auto s_tag, int j) {
@@ -696,10 +739,15 @@ void fa_fwd_h_kernel(Params p) {
         constexpr int GPT = D / 64;                       // score slices per 32-key sub-tile
         constexpr int NPV = PV ? 2 * NKB : 0;
         constexpr int NSL = NPV + (SC ? NKB * GPT : 0);
+        constexpr SliceOrder<NPV, NSL - NPV> ord{};
+        // the MFMA wave of a SIMD takes issue priority; the softmax wave
+        // sharing the SIMD fills the gaps
+        __builtin_amdgcn_s_setprio(3);
         const lds_char* vs = (const lds_char*)smem + 2 * TILE + ((j - 1) & 1) * TILE;
         const char* ks = smem + (j & 1) * TILE;
         frag buf[2][4];
-        auto load = [&](int i) {
+        auto load = [&](int pos) {
+            const int i = ord.v[pos];
             if (i < NPV) {
                 const int rowb = ((i >> 1) * 32 + 16 * (i & 1)) * P;
 #pragma unroll
@@ -707,19 +755,20 @@ void fa_fwd_h_kernel(Params p) {
                     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + voff[dt]));
                     const v4i16 hi =
                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + 8 * P + voff[dt]));
-                    buf[i & 1][dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    buf[pos & 1][dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
             } else {
                 const int g = i - NPV, kt = g / GPT, s0 = 4 * (g % GPT);
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
-                    buf[i & 1][x] = __builtin_bit_cast(frag, ld16(ks + kt * 32 * P + koff[s0 + x]));
+                    buf[pos & 1][x] = __builtin_bit_cast(frag, ld16(ks + kt * 32 * P + koff[s0 + x]));
             }
         };
-        auto exec = [&](int i) {
+        auto exec = [&](int pos) {
+            const int i = ord.v[pos];
             if (i < NPV) {
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = Ty<T>::mma(buf[i & 1][dt], pf[i >> 1][i & 1], oacc[dt]);
+                for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = Ty<T>::mma(buf[pos & 1][dt], pf[i >> 1][i & 1], oacc[dt]);
             } else {
                 const int g = i - NPV, kt = g / GPT, s0 = 4 * (g % GPT);
                 if (s0 == 0) {
@@ -727,15 +776,26 @@ void fa_fwd_h_kernel(Params p) {
                     for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
                 }
 #pragma unroll
-                for (int x = 0; x < 4; ++x) sacc[kt] = Ty<T>::mma(buf[i & 1][x], qf[s0 + x], sacc[kt]);
+                for (int x = 0; x < 4; ++x) sacc[kt] = Ty<T>::mma(buf[pos & 1][x], qf[s0 + x], sacc[kt]);
             }
         };
         load(0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NSL; ++i) {
-            if (i + 1 < NSL) load(i + 1);
+            const bool more = i + 1 < NSL;
+            if (more) load(i + 1);
             exec(i);
+            mfeed(j, i, NSL);
+            if (more) {
+                const int rd = ord.v[i + 1] < NPV ? 2 : 1;    // LDS reads per MFMA
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+                    if (rd == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then LDS reads
+                    else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -744,6 +804,7 @@ void fa_fwd_h_kernel(Params p) {
     auto softmax_run = [&](auto mask_tag, int j) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int kb = j * BC;
+        __builtin_amdgcn_s_setprio(0);
         if constexpr (MASK) {
             // register r of sub-tile kt holds key kb + 4*hf + c with the
             // constant c = 32*kt + 8*(r/4) + r%4; the key is masked when it is
@@ -761,14 +822,15 @@ void fa_fwd_h_kernel(Params p) {
         for (int kt = 0; kt < NKB; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-        const float m_new = fmaxf(m_raw, pair_max(mx));
-        // exponent reference: scale*m_new in log2 units (0 while no key is seen)
-        const float ref = (m_new == -INFINITY) ? 0.f : m_new * p.c;
-        const float alpha = __builtin_amdgcn_exp2f(mc - ref);
-        m_raw = m_new;
-        mc = ref;
+        // running max mc in scaled log2 units (-inf while no key is seen);
+        // O and l are rescaled only in waves where some row's max moved
+        const float cand = pair_max(mx) * p.c;
+        const bool bump = cand > mc;
+        const float alpha = bump ? __builtin_amdgcn_exp2f(mc - cand) : 1.f;
+        mc = bump ? cand : mc;
+        const float ref = (mc == -INFINITY) ? 0.f : mc;
         lsum *= alpha;
-        if (__ballot(alpha != 1.f)) {
+        if (__ballot(bump)) {
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -788,19 +850,6 @@ void fa_fwd_h_kernel(Params p) {
             }
     };
 
-    // Group 1 issues every DMA, in its softmax phases, which leaves the MFMA
-    // phases free of memory-instruction issue: the DMA for K_{t+1} and V_t
-    // goes out at the start of phase 2t (group 1's X(t-1), or its first, idle
-    // phase for t = 0) and is waited for at the end of phase 2t+1 (group 1's
-    // M(t)); the barrier there publishes the stages.
-    const bool feeder = group == 1;
-    auto dma_tile = [&](int t) {                  // K_{t+1}, V_t
-        if (t + 1 < ntiles) issue_k2(t + 1);
-        issue_v2(t);
-    };
-    auto start_x = [&](int j) {                   // start of X(j) = phase 2j+2 (group 1)
-        if (feeder && j + 1 < ntiles) dma_tile(j + 1);
-    };
     // The softmax phase's results are consumed only in the next MFMA phase, so
     // the compiler would sink the exp / convert / sum work past the barrier
     // into it.  An empty asm that "modifies" them pins that work here.
@@ -809,20 +858,20 @@ void fa_fwd_h_kernel(Params p) {
         for (int kt = 0; kt < NKB; ++kt)
 #pragma unroll
             for (int ps = 0; ps < 2; ++ps) asm volatile("" : "+v"(pf[kt][ps]));
-        asm volatile("" : "+v"(lsum), "+v"(mc), "+v"(m_raw));
+        asm volatile("" : "+v"(lsum), "+v"(mc));
     };
     // phase boundaries: the scheduling barriers keep the compiler from
     // moving register-only work (row max, MFMAs) across the workgroup barrier,
     // which would undo the phase split
     auto end_m = [&]() {
         __builtin_amdgcn_sched_barrier(0);
-        if (feeder) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
     auto end_x = [&]() {
         pin_x();
         __builtin_amdgcn_sched_barrier(0);
+        if (feeder) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -832,48 +881,37 @@ void fa_fwd_h_kernel(Params p) {
     if (feeder) issue_k2(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (feeder) {                                 // group 1's first phase: DMA only
-        dma_tile(0);
-        __syncthreads();
-    }
+    if (group == 1) __syncthreads();              // group 1 starts one phase later
     int j = 0;
     if (ntw > 0) {
         mma_run(no{}, yes{}, 0);
         end_m();
-        start_x(0);
         if (jmask == 0) softmax_run(yes{}, 0);
         else softmax_run(no{}, 0);
         end_x();
         for (j = 1; j < min(jmask, ntw); ++j) {   // steady state, no masking
             mma_run(yes{}, yes{}, j);
             end_m();
-            start_x(j);
             softmax_run(no{}, j);
             end_x();
         }
         for (j = max(j, 1); j < ntw; ++j) {      // tiles that need the mask
             mma_run(yes{}, yes{}, j);
             end_m();
-            start_x(j);
             softmax_run(yes{}, j);
             end_x();
         }
         mma_run(yes{}, no{}, j);                  // j == ntw: last PV
         end_m();
-        if (j < ntiles) {
-            start_x(j);
-            end_x();
-        }
+        if (j < ntiles) end_x();
         ++j;
     }
     for (; j <= ntiles; ++j) {                    // phases of tiles this wave does not need
+        if (feeder && j < ntiles) dma_tile(j);
         end_m();
-        if (j < ntiles) {
-            start_x(j);
-            end_x();
-        }
+        if (j < ntiles) end_x();
     }
-    if (!feeder) __syncthreads();                 // group 0 ends one phase later
+    if (group == 0) __syncthreads();              // group 0 ends one phase later
 
     // epilogue: one division by l, logsumexp, stores
     const float ltot = pair_sum(lsum);
