@@ -519,6 +519,12 @@ __device__ inline i32x4 buffer_rsrc(const void* base, int bytes) {
     return r;
 }
 
+// The same buffer advanced by `off` bytes (off a multiple of 16): offsets
+// are checked against what is left, so reads past the end still return 0.
+__device__ inline i32x4 buffer_rsrc_at(const char* base, int bytes, int off) {
+    return buffer_rsrc(base + off, max(bytes - off, 0));
+}
+
 // 16 bytes per lane from buffer offset `voff` into LDS at lds_base + 16*lane
 // (buffer_load_dwordx4 ... lds).  Issued as inline asm so that the compiler's
 // wait-count insertion does not make later LDS reads wait for this DMA: the
@@ -616,8 +622,9 @@ void fa_fwd_h_kernel(Params p) {
     const int hf = lane >> 5;
     const long long head = (long long)bh * L * D;
     const char* qh = p.q + head * 2;
-    const i32x4 krs = buffer_rsrc(p.k + head * 2, L * P);
-    const i32x4 vrs = buffer_rsrc(p.v + head * 2, L * P);
+    const char* kh = p.k + head * 2;
+    const char* vh = p.v + head * 2;
+    const i32x4 krs = buffer_rsrc(kh, L * P);
 
     const int q0 = qt * BR;
     const int qw = q0 + wave * QPW;                 // this wave's first query row
@@ -673,14 +680,14 @@ void fa_fwd_h_kernel(Params p) {
     int koff[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) koff[s] = l32 * P + (((2 * s + hf) ^ Lay::fk(l32)) << 4);
-    int voff[D / 32];
+    int voffv[D / 32];
     {
         const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
         const int rrel = 4 * (g >> 1) + e;            // key row within an 8-key group
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
             const int c = 4 * dt + 2 * (g & 1) + (q >> 1);
-            voff[dt] = rrel * P + ((c ^ Lay::fv(rrel)) << 4) + 8 * (q & 1);
+            voffv[dt] = 2 * TILE + rrel * P + ((c ^ Lay::fv(rrel)) << 4) + 8 * (q & 1);   // V stages start at 2*TILE
         }
     }
 
@@ -702,14 +709,15 @@ void fa_fwd_h_kernel(Params p) {
     constexpr int NPIECE = 4 * LPW;               // DMA instructions per wave for K_{t+1}, V_t
     auto dma_piece = [&](int t, int n) {          // n-th instruction of K_{t+1}, V_t
         const int x = (n >> 1) % LPW, hi = n & 1;
+        // the descriptors move to the tile, so the per-lane offsets are loop-invariant
         if (n < 2 * LPW) {
             if (t + 1 < ntiles) {
                 const unsigned dst = lds0 + ((t + 1) & 1) * TILE + 1024 * (wq * LPW + x) + hi * 4096 * LPW;
-                dma16(krs, kdma_off(x, hi) + (t + 1) * TILE, __builtin_amdgcn_readfirstlane(dst));
+                dma16(buffer_rsrc_at(kh, L * P, (t + 1) * TILE), kdma_off(x, hi), __builtin_amdgcn_readfirstlane(dst));
             }
         } else {
             const unsigned dst = lds0 + 2 * TILE + (t & 1) * TILE + 1024 * (wq * LPW + x) + hi * 4096 * LPW;
-            dma16(vrs, vdma_off(x, hi) + t * TILE, __builtin_amdgcn_readfirstlane(dst));
+            dma16(buffer_rsrc_at(vh, L * P, t * TILE), vdma_off(x, hi), __builtin_amdgcn_readfirstlane(dst));
         }
     };
     auto dma_tile = [&](int t) {                  // all of K_{t+1}, V_t at once (phases without MFMAs)
@@ -733,9 +741,15 @@ void fa_fwd_h_kernel(Params p) {
     // so that reads neither queue behind a burst nor land just before use.
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
-    auto mma_run = [&](auto pv_tag, auto s_tag, int j) {
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using PR = std::integral_constant<int, -1>;
+    // par_tag: K/V stage parity of tile j when known at compile time (0/1),
+    // else -1; a known parity folds the stage offsets into the LDS reads
+    auto mma_run = [&](auto pv_tag, auto s_tag, int j, auto par_tag) {
         constexpr bool PV = decltype(pv_tag)::value;
         constexpr bool SC = decltype(s_tag)::value;
+        constexpr int PAR = decltype(par_tag)::value;
         constexpr int GPT = D / 64;                       // score slices per 32-key sub-tile
         constexpr int NPV = PV ? 2 * NKB : 0;
         constexpr int NSL = NPV + (SC ? NKB * GPT : 0);
@@ -743,8 +757,9 @@ void fa_fwd_h_kernel(Params p) {
         // the MFMA wave of a SIMD takes issue priority; the softmax wave
         // sharing the SIMD fills the gaps
         __builtin_amdgcn_s_setprio(3);
-        const lds_char* vs = (const lds_char*)smem + 2 * TILE + ((j - 1) & 1) * TILE;
-        const char* ks = smem + (j & 1) * TILE;
+        const int kst = PAR >= 0 ? PAR : (j & 1);
+        const lds_char* vs = (const lds_char*)smem + (1 - kst) * TILE;    // voffv holds the 2*TILE
+        const char* ks = smem + kst * TILE;
         frag buf[2][4];
         auto load = [&](int pos) {
             const int i = ord.v[pos];
@@ -752,9 +767,9 @@ void fa_fwd_h_kernel(Params p) {
                 const int rowb = ((i >> 1) * 32 + 16 * (i & 1)) * P;
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
-                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + voff[dt]));
+                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + voffv[dt]));
                     const v4i16 hi =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + 8 * P + voff[dt]));
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + 8 * P + voffv[dt]));
                     buf[pos & 1][dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
             } else {
@@ -884,24 +899,38 @@ void fa_fwd_h_kernel(Params p) {
     if (group == 1) __syncthreads();              // group 1 starts one phase later
     int j = 0;
     if (ntw > 0) {
-        mma_run(no{}, yes{}, 0);
+        mma_run(no{}, yes{}, 0, P0{});
         end_m();
         if (jmask == 0) softmax_run(yes{}, 0);
         else softmax_run(no{}, 0);
         end_x();
-        for (j = 1; j < min(jmask, ntw); ++j) {   // steady state, no masking
-            mma_run(yes{}, yes{}, j);
+        // steady state, no masking; two tiles per trip so that the stage
+        // parity (odd j first) is a constant in each half
+        const int jsteady = min(jmask, ntw);
+        for (j = 1; j + 1 < jsteady; j += 2) {
+            mma_run(yes{}, yes{}, j, P1{});
             end_m();
             softmax_run(no{}, j);
             end_x();
+            mma_run(yes{}, yes{}, j + 1, P0{});
+            end_m();
+            softmax_run(no{}, j + 1);
+            end_x();
+        }
+        if (j < jsteady) {
+            mma_run(yes{}, yes{}, j, P1{});
+            end_m();
+            softmax_run(no{}, j);
+            end_x();
+            ++j;
         }
         for (j = max(j, 1); j < ntw; ++j) {      // tiles that need the mask
-            mma_run(yes{}, yes{}, j);
+            mma_run(yes{}, yes{}, j, PR{});
             end_m();
             softmax_run(yes{}, j);
             end_x();
         }
-        mma_run(yes{}, no{}, j);                  // j == ntw: last PV
+        mma_run(yes{}, no{}, j, PR{});                  // j == ntw: last PV
         end_m();
         if (j < ntiles) end_x();
         ++j;
