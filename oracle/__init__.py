@@ -9,6 +9,9 @@ Contents
   * ``fwd``   -- the plain definition (materialised score row, safe softmax,
                  weighted sum, logsumexp) in C, float64, OpenMP over rows.
   * ``brute`` -- a separate C brute-force twin for tiny shapes.
+  * ``attn_range`` / ``merge`` -- one K/V block's attention for a few query
+                 rows (rectangular, no mask) and the merge of such partial
+                 results: the Flash-Decoding task and its combine step.
   * ``tiled`` -- float64 NumPy models of the tiled online-softmax algorithm
                  itself, used only to pin that the tiled method is exact.
 
@@ -51,6 +54,10 @@ def _load():
         lib.fa_oracle_fwd.restype = i
         lib.fa_oracle_brute.argtypes = [vp, vp, vp, i, i, i, i, d, i, vp, vp]
         lib.fa_oracle_brute.restype = i
+        lib.fa_oracle_range.argtypes = [vp, vp, vp, i, i, i, i, i, i, d, i, i, vp, vp, i]
+        lib.fa_oracle_range.restype = i
+        lib.fa_oracle_merge.argtypes = [vp, vp, i, i, i, vp, vp]
+        lib.fa_oracle_merge.restype = i
         lib.fa_oracle_max_threads.argtypes = []
         lib.fa_oracle_max_threads.restype = i
         _lib = lib
@@ -108,4 +115,44 @@ def brute(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: int
                                  o.ctypes.data, lse.ctypes.data)
     if rc != 0:
         raise ValueError(f"fa_oracle_brute rejected its arguments (rc={rc})")
+    return o, lse
+
+
+def attn_range(q, k, v, dtype: int, scale: float, kv_begin: int, kv_end: int, nthreads: int = 0):
+    """O (B,H,Lq,d) and lse (B,H,Lq), float64, of q (B,H,Lq,d) against keys
+    [kv_begin, kv_end) of k, v (B,H,Lk,d).  Empty range: O = 0, lse = -inf."""
+    q = _storage_check(q, dtype)
+    k = _storage_check(k, dtype)
+    v = _storage_check(v, dtype)
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if k.shape != (B, H, Lk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be (B, H, Lk, d) matching q")
+    o = np.empty((B, H, Lq, d), dtype=np.float64)
+    lse = np.empty((B, H, Lq), dtype=np.float64)
+    rc = _load().fa_oracle_range(q.ctypes.data, k.ctypes.data, v.ctypes.data, dtype,
+                                 B, H, Lq, Lk, d, float(scale), int(kv_begin), int(kv_end),
+                                 o.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"fa_oracle_range rejected its arguments (rc={rc})")
+    return o, lse
+
+
+def merge(o_parts, lse_parts):
+    """Merge partial results: o_parts (S, ..., d), lse_parts (S, ...) float64
+    -> o (..., d), lse (...)."""
+    o_parts = np.ascontiguousarray(o_parts, dtype=np.float64)
+    lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    S = o_parts.shape[0]
+    d = o_parts.shape[-1]
+    rows_shape = o_parts.shape[1:-1]
+    if lse_parts.shape != (S,) + rows_shape:
+        raise ValueError("lse_parts must be o_parts' shape without its last axis")
+    n = int(np.prod(rows_shape)) if rows_shape else 1
+    o = np.empty(rows_shape + (d,), dtype=np.float64)
+    lse = np.empty(rows_shape, dtype=np.float64)
+    rc = _load().fa_oracle_merge(o_parts.ctypes.data, lse_parts.ctypes.data, S, n, d,
+                                 o.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"fa_oracle_merge rejected its arguments (rc={rc})")
     return o, lse

@@ -174,3 +174,85 @@ int fa_oracle_brute(const double* q, const double* k, const double* v,
     }
     return 0;
 }
+
+/* ---- one K/V block's attention, rectangular (Flash-Decoding task) ---- */
+
+int fa_oracle_range(const void* q, const void* k, const void* v, int dtype,
+                    int B, int H, int Lq, int Lk, int d, double scale,
+                    int kv_begin, int kv_end, double* o, double* lse, int nthreads) {
+    if (!q || !k || !v || !o || !lse) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16 && dtype != ORACLE_F64)
+        return -1;
+    if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || d <= 0) return -1;
+    if (kv_begin < 0 || kv_end < kv_begin || kv_end > Lk) return -1;
+    if (nthreads <= 0) nthreads = fa_oracle_max_threads();
+    const int n = kv_end - kv_begin;
+
+    for (int bh = 0; bh < B * H; ++bh) {
+        const size_t qbase = (size_t)bh * Lq * d;
+        const size_t kbase = (size_t)bh * Lk * d;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+        for (int i = 0; i < Lq; ++i) {
+            double* oi = o + qbase + (size_t)i * d;
+            for (int c = 0; c < d; ++c) oi[c] = 0.0;
+            if (n == 0) {
+                lse[(size_t)bh * Lq + i] = -INFINITY;
+                continue;
+            }
+            double* s = (double*)malloc((size_t)n * sizeof(double));
+            /* score row over the block's keys */
+            for (int j = 0; j < n; ++j) {
+                double dot = 0.0;
+                for (int c = 0; c < d; ++c)
+                    dot += widen(q, dtype, qbase + (size_t)i * d + c) *
+                           widen(k, dtype, kbase + (size_t)(kv_begin + j) * d + c);
+                s[j] = scale * dot;
+            }
+            double m = -INFINITY;
+            for (int j = 0; j < n; ++j)
+                if (s[j] > m) m = s[j];
+            double l = 0.0;
+            for (int j = 0; j < n; ++j) {
+                s[j] = exp(s[j] - m); /* s now holds p */
+                l += s[j];
+            }
+            for (int j = 0; j < n; ++j)
+                for (int c = 0; c < d; ++c) oi[c] += s[j] * widen(v, dtype, kbase + (size_t)(kv_begin + j) * d + c);
+            for (int c = 0; c < d; ++c) oi[c] /= l;
+            lse[(size_t)bh * Lq + i] = m + log(l);
+            free(s);
+        }
+    }
+    return 0;
+}
+
+/* ---- merge of per-block results ---- */
+
+int fa_oracle_merge(const double* o_parts, const double* lse_parts, int nsplit, int n, int d,
+                    double* o, double* lse) {
+    if (!o_parts || !lse_parts || !o || !lse) return -1;
+    if (nsplit <= 0 || n <= 0 || d <= 0) return -1;
+    for (int r = 0; r < n; ++r) {
+        double mx = -INFINITY;
+        for (int t = 0; t < nsplit; ++t) {
+            const double x = lse_parts[(size_t)t * n + r];
+            if (x > mx) mx = x;
+        }
+        double* orow = o + (size_t)r * d;
+        for (int c = 0; c < d; ++c) orow[c] = 0.0;
+        if (mx == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double wsum = 0.0;
+        for (int t = 0; t < nsplit; ++t) wsum += exp(lse_parts[(size_t)t * n + r] - mx);
+        const double total = mx + log(wsum);
+        for (int t = 0; t < nsplit; ++t) {
+            const double w = exp(lse_parts[(size_t)t * n + r] - total);
+            const double* op = o_parts + ((size_t)t * n + r) * d;
+            for (int c = 0; c < d; ++c) orow[c] += w * op[c];
+        }
+        lse[r] = total;
+    }
+    return 0;
+}

@@ -56,6 +56,38 @@ int fa_oracle_brute(const double* q, const double* k, const double* v,
                     int B, int H, int L, int d, double scale, int causal,
                     double* o, double* lse);
 
+/*
+ * Attention of Lq query rows against the keys [kv_begin, kv_end) of a head
+ * with Lk keys (no mask): the same definition as fa_oracle_fwd on a
+ * rectangular score block.  This is one K/V block's task in Flash-Decoding
+ * ("04 Transformers, Attention, and FlashAttention", the Flash Decoding
+ * steps: split K/V into blocks, run each as a small attention task, merge).
+ * q : (B, H, Lq, d); k, v : (B, H, Lk, d), storage type `dtype`.
+ * o : float64 (B, H, Lq, d); lse : float64 (B, H, Lq).
+ * An empty range (kv_begin == kv_end) has no keys: l = 0, so by convention
+ * o = 0 and lse = -inf (the neutral element of the merge below).
+ * Returns 0, or -1 on a bad argument (nothing written).
+ */
+int fa_oracle_range(const void* q, const void* k, const void* v, int dtype,
+                    int B, int H, int Lq, int Lk, int d, double scale,
+                    int kv_begin, int kv_end, double* o, double* lse, int nthreads);
+
+/*
+ * Merge of attention results over disjoint key sets (the third Flash
+ * Decoding step).  For each of n rows, part s holds its normalised output
+ * o_s (d values) and lse_s = m_s + ln l_s.  The pages' rescale rule
+ * (running max m, sum rescaled by exp(m_old - m_new), "FlashAttention
+ * 深度解析" first article, online softmax) applied to the parts gives
+ *     lse = ln sum_s exp(lse_s),   o = sum_s exp(lse_s - lse) o_s,
+ * evaluated here with the largest lse_s as the shift.  Parts with
+ * lse_s = -inf contribute nothing; if every part is empty, o = 0 and
+ * lse = -inf.
+ * o_parts : float64 (nsplit, n, d); lse_parts : float64 (nsplit, n).
+ * o : float64 (n, d); lse : float64 (n).  Returns 0, or -1 on a bad argument.
+ */
+int fa_oracle_merge(const double* o_parts, const double* lse_parts, int nsplit, int n, int d,
+                    double* o, double* lse);
+
 /* Threads an fa_oracle_fwd call with nthreads <= 0 would use. */
 int fa_oracle_max_threads(void);
 
