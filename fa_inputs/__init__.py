@@ -29,7 +29,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from .configs import CONFIGS, Config, config  # noqa: F401
+from .configs import CONFIGS, DECODE, Config, DecodeConfig, config  # noqa: F401
 
 F32, F16, BF16 = 0, 1, 2
 DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
@@ -174,4 +174,12 @@ def make_qkv(cfg: "Config"):
     q = fill(cfg.dtype, shape, cfg.seed, 0, cfg.sigma_q)
     k = fill(cfg.dtype, shape, cfg.seed, 1, cfg.sigma_k)
     v = fill(cfg.dtype, shape, cfg.seed, 2, cfg.sigma_v)
+    return q, k, v
+
+
+def make_decode_qkv(cfg):
+    """Q (B, H, Lq, d) and K, V (B, H, Lk, d) storage arrays for a decoding shape."""
+    q = fill(cfg.dtype, (cfg.B, cfg.H, cfg.Lq, cfg.d), cfg.seed, 0, cfg.sigma_q)
+    k = fill(cfg.dtype, (cfg.B, cfg.H, cfg.Lk, cfg.d), cfg.seed, 1, cfg.sigma_k)
+    v = fill(cfg.dtype, (cfg.B, cfg.H, cfg.Lk, cfg.d), cfg.seed, 2, cfg.sigma_v)
     return q, k, v

@@ -60,3 +60,39 @@ CONFIGS = [
 
 def config(index: int) -> Config:
     return CONFIGS[index]
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    """A decoding shape for the split-K/V path: Lq query rows per (b, h)
+    against a cache of Lk keys (no mask)."""
+    name: str
+    B: int
+    H: int
+    Lq: int
+    Lk: int
+    d: int
+    dtype: int
+    scale: float
+    seed: int
+    sigma_q: float = 1.0
+    sigma_k: float = 1.0
+    sigma_v: float = 1.0
+
+    @property
+    def flops(self) -> int:
+        """4*B*H*Lq*Lk*d (both products)."""
+        return 4 * self.B * self.H * self.Lq * self.Lk * self.d
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once, O written once, lse (fp32) written once."""
+        eb = 4 if self.dtype == 0 else 2
+        bh = self.B * self.H
+        return bh * (2 * self.Lq + 2 * self.Lk) * self.d * eb + 4 * bh * self.Lq
+
+
+# Decoding with a long K/V cache: one new query row per (batch, head), 1 GiB
+# of K/V in bf16.  Seed 10; streams 0/1/2 are Q/K/V.
+DECODE = DecodeConfig("decode bf16 B8 H32 Lq1 Lk16384 d128", 8, 32, 1, 16384, 128, 2,
+                      1.0 / math.sqrt(128.0), 10)

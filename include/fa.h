@@ -21,6 +21,8 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
+
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -88,6 +90,82 @@ int fa_last_hip_error(void);
  * for (B, H, L).  Returns FA_OK or an argument error as fa_fwd would. */
 int fa_fwd_tiling(int B, int H, int L, int d, int causal, int dtype,
                   int* block_rows, int* block_cols, long long* workgroups);
+
+/*
+ * ---- Split-K/V attention for few query rows (decoding) ----
+ *
+ * Flash-Decoding ("04 Transformers, Attention, and FlashAttention", the
+ * Flash Decoding steps): with only a handful of query rows per head there is
+ * not enough query parallelism, so the keys of each (batch, head) are cut into
+ * nsplit contiguous chunks, each chunk is attended to as its own small
+ * attention task (partial output O_s, normalised by its own sum, and its
+ * logsumexp lse_s), and the chunks are merged with the online-softmax rescale
+ * rule ("FlashAttention 深度解析", first article: statistics brought to a
+ * common maximum by exp(m_old - m_new) and added):
+ *     lse = ln sum_s exp(lse_s),    O = sum_s exp(lse_s - lse) O_s.
+ * The result is the same attention as fa_fwd with causal = 0, for a query
+ * block of Lq rows against Lk keys: the softmax over all Lk keys.
+ */
+
+/*
+ * fa_splitkv_splits -- the nsplit that fa_fwd_splitkv uses when passed
+ * nsplit <= 0: enough chunks to occupy the GPU, at least 256 keys each.
+ * Returns 0 for non-positive sizes.
+ */
+int fa_splitkv_splits(int B, int H, int Lk);
+
+/*
+ * fa_splitkv_workspace_bytes -- device workspace fa_fwd_splitkv needs for
+ * these sizes (nsplit <= 0: the automatic choice).  Returns 0 for
+ * non-positive sizes or d not 64/128.
+ */
+size_t fa_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int nsplit);
+
+/*
+ * fa_fwd_splitkv -- enqueue split-K/V attention and the merge on `stream`.
+ *
+ * q, o    : device, (B, H, Lq, d) contiguous row-major, d fastest; o fully
+ *           overwritten with the attention output in the storage type.
+ * k, v    : device, (B, H, Lk, d) in the same layout and type; read only.
+ * lse     : device float32 (B, H, Lq); fully overwritten (natural log).
+ * Lq      : query rows per (b, h), 1..8 (more rows: use fa_fwd).
+ * Lk      : keys per (b, h), >= 1.  No mask: every query sees every key.
+ * d, scale, dtype : as for fa_fwd.
+ * nsplit  : chunks per (b, h); <= 0 picks fa_splitkv_splits(B, H, Lk).
+ *           Chunk s covers keys [s*c, min((s+1)*c, Lk)) with c = ceil(Lk/nsplit);
+ *           chunks past the end are empty and merge as no contribution.
+ * workspace, workspace_size : device scratch of at least
+ *           fa_splitkv_workspace_bytes(B, H, Lq, Lk, d, nsplit) bytes,
+ *           256-byte aligned, owned by the caller; it holds the partial results
+ *           (float32 O_s (nsplit, B, H, Lq, d), then float32 lse_s
+ *           (nsplit, B, H, Lq), each padded to 256 bytes) until the merge on
+ *           the same stream has read them.  Calls sharing a workspace must be
+ *           ordered on one stream.
+ * The arithmetic is fp32 throughout (no rounding of P), and the output is
+ * rounded once to the storage type.
+ * Ownership, asynchrony and errors as for fa_fwd.  Lq > 8 returns
+ * FA_ERR_UNSUPPORTED; a small workspace, B*H > 65535 or nsplit > 262140
+ * returns FA_ERR_INVALID_ARG; a workspace not 256-byte aligned returns
+ * FA_ERR_ALIGN.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Lq, int Lk, int d, float scale, int dtype, int nsplit,
+                   void* workspace, size_t workspace_size, hipStream_t stream);
+
+/*
+ * fa_combine -- enqueue only the merge of nsplit partial results.
+ *
+ * o_part   : device float32 (nsplit, B, H, Lq, d): normalised partial outputs.
+ * lse_part : device float32 (nsplit, B, H, Lq): their logsumexp; -inf marks a
+ *            part with no keys (its o_part row is ignored).
+ * o        : device (B, H, Lq, d) in `dtype`; lse : device float32 (B, H, Lq).
+ *            A row whose parts are all empty gets o = 0 and lse = -inf.
+ * Lq here may be any positive count (the merge is per row).  Ownership,
+ * asynchrony and errors as for fa_fwd (o 16-byte aligned, the float arrays
+ * 4-byte aligned).
+ */
+int fa_combine(const float* o_part, const float* lse_part, int nsplit, int B, int H, int Lq, int d,
+               void* o, float* lse, int dtype, hipStream_t stream);
 
 #ifdef __cplusplus
 }

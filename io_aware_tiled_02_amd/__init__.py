@@ -41,6 +41,14 @@ def load():
         lib.fa_fwd_tiling.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
                                       ctypes.POINTER(ctypes.c_longlong)]
         lib.fa_fwd_tiling.restype = i
+        lib.fa_splitkv_splits.argtypes = [i, i, i]
+        lib.fa_splitkv_splits.restype = i
+        lib.fa_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+        lib.fa_fwd_splitkv.restype = i
+        lib.fa_combine.argtypes = [vp, vp, i, i, i, i, i, vp, vp, i, vp]
+        lib.fa_combine.restype = i
         _lib = lib
     return _lib
 
@@ -48,6 +56,26 @@ def load():
 def fa_fwd(q, k, v, o, lse, B, H, L, d, scale, causal, dtype, stream) -> int:
     """The C entry point as is: raw device addresses (ints) and a raw stream handle."""
     return load().fa_fwd(q, k, v, o, lse, B, H, L, d, scale, causal, dtype, stream)
+
+
+def fa_splitkv_splits(B, H, Lk) -> int:
+    return load().fa_splitkv_splits(B, H, Lk)
+
+
+def fa_splitkv_workspace_bytes(B, H, Lq, Lk, d, nsplit) -> int:
+    return load().fa_splitkv_workspace_bytes(B, H, Lq, Lk, d, nsplit)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, workspace, workspace_size,
+                   stream) -> int:
+    """The C entry point as is (raw device addresses and stream handle)."""
+    return load().fa_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, workspace,
+                                 workspace_size, stream)
+
+
+def fa_combine(o_part, lse_part, nsplit, B, H, Lq, d, o, lse, dtype, stream) -> int:
+    """The C entry point as is (raw device addresses and stream handle)."""
+    return load().fa_combine(o_part, lse_part, nsplit, B, H, Lq, d, o, lse, dtype, stream)
 
 
 def fa_strerror(code: int) -> str:
@@ -98,6 +126,40 @@ def forward(q, k, v, scale: float, causal: bool = False, out=None, lse=None, str
         stream = torch.cuda.current_stream(q.device)
     rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                 B, H, L, d, float(scale), int(bool(causal)), _dtype_code(q), stream.cuda_stream)
+    if rc != FA_OK:
+        raise FAError(rc, fa_strerror(rc))
+    return out, lse
+
+
+def forward_splitkv(q, k, v, scale: float, nsplit: int = 0, out=None, lse=None, workspace=None, stream=None):
+    """Split-K/V attention of q (B, H, Lq, d) against k, v (B, H, Lk, d), Lq <= 8.
+
+    The workspace (a uint8 device tensor) is allocated with torch unless given.
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q is (B, H, Lq, d); k and v share one (B, H, Lk, d) shape")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError("q and k/v disagree on B, H or d")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    need = fa_splitkv_workspace_bytes(B, H, Lq, Lk, d, nsplit)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, Lq, Lk, d, float(scale), _dtype_code(q), int(nsplit), workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(), stream.cuda_stream)
     if rc != FA_OK:
         raise FAError(rc, fa_strerror(rc))
     return out, lse

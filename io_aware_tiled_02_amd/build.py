@@ -6,7 +6,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "fa_fwd.hip")
+SRCS = [os.path.join(HERE, "csrc", "fa_fwd.hip"), os.path.join(HERE, "csrc", "fa_splitkv.hip")]
 LIB = os.path.join(HERE, "libfa_fwd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -19,9 +19,9 @@ FLAGS = [
 ]
 
 
-def build(extra_flags=None, src: str = SRC, out: str = LIB, verbose: bool = False) -> str:
+def build(extra_flags=None, srcs=None, out: str = LIB, verbose: bool = False) -> str:
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), src, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *(extra_flags or []), *(srcs or SRCS), "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)

@@ -45,6 +45,20 @@
 #include <type_traits>
 
 #include "fa.h"
+#include "fa_internal.h"
+
+namespace fa_detail {
+thread_local int g_last_hip = 0;
+
+int launch_status() {
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+        g_last_hip = (int)err;
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+}
+}  // namespace fa_detail
 
 namespace {
 
@@ -963,7 +977,6 @@ void fa_fwd_h_kernel(Params p) {
 
 // ---- host side ----
 
-thread_local int g_last_hip = 0;
 
 struct Tiling {
     int br, bc;
@@ -1002,14 +1015,7 @@ inline Params make_params(const void* q, const void* k, const void* v, void* o, 
     return p;
 }
 
-inline int launch_status() {
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) {
-        g_last_hip = (int)err;
-        return FA_ERR_HIP;
-    }
-    return FA_OK;
-}
+inline int launch_status() { return fa_detail::launch_status(); }
 
 template <class T, int D, bool CAUSAL>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int L, float scale,
@@ -1103,7 +1109,7 @@ extern "C" const char* fa_strerror(int status) {
     }
 }
 
-extern "C" int fa_last_hip_error(void) { return g_last_hip; }
+extern "C" int fa_last_hip_error(void) { return fa_detail::g_last_hip; }
 
 extern "C" int fa_fwd_tiling(int B, int H, int L, int d, int causal, int dtype, int* block_rows, int* block_cols,
                              long long* workgroups) {

@@ -68,3 +68,61 @@ def test_tiling_query():
     assert wg == 32 * ((8192 + br - 1) // br)
     with pytest.raises(fa.FAError):
         fa.fa_fwd_tiling(1, 1, 64, 80, 0, fa.FA_BF16)
+
+
+# ---- split-K/V entry points ---------------------------------------------------
+
+W = 1 << 24   # fake 256-byte-aligned workspace address
+BIG = 1 << 40
+
+
+def _sk(**kw):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=4, Lq=1, Lk=1000, d=128, scale=0.1, dtype=2, nsplit=4,
+             ws=W, wsz=BIG, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Lq"], a["Lk"], a["d"],
+                             a["scale"], a["dtype"], a["nsplit"], a["ws"], a["wsz"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Lq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Lk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Lq=9), fa.FA_ERR_UNSUPPORTED),        # more than 8 query rows: fa_fwd's job
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(B=300, H=300), fa.FA_ERR_INVALID_ARG),  # B*H over one grid dimension
+    (dict(nsplit=4 * 65535 + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(q=A + 8), fa.FA_ERR_ALIGN),
+    (dict(ws=W + 16), fa.FA_ERR_ALIGN),          # workspace must be 256-byte aligned
+    (dict(wsz=1024), fa.FA_ERR_INVALID_ARG),      # workspace too small
+])
+def test_splitkv_argument_errors(kw, want):
+    assert _sk(**kw) == want
+
+
+def test_splitkv_workspace_size_and_auto_splits():
+    # 4 splits x 8 rows x 128 floats (4096 B) + 4 x 8 floats padded to 256 B
+    assert fa.fa_splitkv_workspace_bytes(2, 4, 1, 1000, 128, 4) == 4 * 8 * 128 * 4 + 256
+    assert _sk(wsz=4 * 8 * 128 * 4 + 255) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_splitkv_workspace_bytes(0, 4, 1, 1000, 128, 4) == 0
+    s = fa.fa_splitkv_splits(1, 32, 32768)
+    assert 1 <= s <= (32768 + 255) // 256 and 32 * s >= 2048
+    assert fa.fa_splitkv_splits(1, 1, 100) == 1                 # at least 256 keys per chunk
+    assert fa.fa_splitkv_workspace_bytes(1, 32, 1, 32768, 128, 0) == \
+        fa.fa_splitkv_workspace_bytes(1, 32, 1, 32768, 128, s)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((0, A, 4, 1, 1, 1, 128, A, A, 2, 0), fa.FA_ERR_INVALID_ARG),
+    ((A, A, 0, 1, 1, 1, 128, A, A, 2, 0), fa.FA_ERR_INVALID_ARG),       # nsplit 0
+    ((A, A, 4, 1, 1, 1, 80, A, A, 2, 0), fa.FA_ERR_UNSUPPORTED),
+    ((A, A, 4, 1, 1, 1, 128, A, A, 7, 0), fa.FA_ERR_UNSUPPORTED),
+    ((A, A, 4, 1, 1, 1, 128, A + 4, A, 2, 0), fa.FA_ERR_ALIGN),
+])
+def test_combine_argument_errors(args, want):
+    assert fa.fa_combine(*args) == want
