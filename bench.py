@@ -90,12 +90,114 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def cpu_baseline_decode(cfg, q, k, v, target_s: float):
+    """The fp64 oracle (key-range attention over all keys) on a bounded sample of heads."""
+    import oracle
+    nth = oracle.max_threads()
+    bh = cfg.B * cfg.H
+    qs = q.reshape(bh, 1, cfg.Lq, cfg.d)
+    ks = k.reshape(bh, 1, cfg.Lk, cfg.d)
+    vs = v.reshape(bh, 1, cfg.Lk, cfg.d)
+    t = time.perf_counter()
+    oracle.attn_range(qs[:2], ks[:2], vs[:2], cfg.dtype, cfg.scale, 0, cfg.Lk)
+    t0 = max(time.perf_counter() - t, 1e-3)
+    nh = int(min(bh, max(2, 2 * target_s / t0)))
+    t = time.perf_counter()
+    oracle.attn_range(qs[:nh], ks[:nh], vs[:nh], cfg.dtype, cfg.scale, 0, cfg.Lk)
+    dt = time.perf_counter() - t
+    eb = 4 if cfg.dtype == gen.F32 else 2
+    nbytes = nh * (2 * cfg.Lq + 2 * cfg.Lk) * cfg.d * eb + 4 * nh * cfg.Lq
+    return {
+        "value": nbytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": min(nth, cfg.Lq),          # the oracle's threads split query rows of one head
+        "kind": "oracle",
+        "sample": (f"{nh} of {bh} (b, h) heads of the same workload, each {cfg.Lq} query row(s) against all "
+                   f"{cfg.Lk} keys, fp64 C oracle (OpenMP over query rows); {dt:.1f} s"),
+        "seconds": dt,
+        "cpu_model": _cpu_model(),
+        "nproc": os.cpu_count(),
+    }
+
+
+def bench_decode(args, torch, fa):
+    """Split-K/V attention (fa_fwd_splitkv: chunk kernel + merge) on the decoding shape."""
+    cfg = gen.DECODE
+    log(f"[bench] decode: {cfg.name}; generating inputs")
+    q, k, v = gen.make_decode_qkv(cfg)
+
+    def dev(a):
+        if cfg.dtype == gen.BF16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(a).to("cuda")
+
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o = torch.empty_like(qd)
+    lse = torch.empty((cfg.B, cfg.H, cfg.Lq), dtype=torch.float32, device="cuda")
+    nsplit = fa.fa_splitkv_splits(cfg.B, cfg.H, cfg.Lk)
+    need = fa.fa_splitkv_workspace_bytes(cfg.B, cfg.H, cfg.Lq, cfg.Lk, cfg.d, nsplit)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), cfg.B, cfg.H, cfg.Lq,
+            cfg.Lk, cfg.d, float(cfg.scale), cfg.dtype, nsplit, ws.data_ptr(), need, stream.cuda_stream)
+    log(f"[bench] warmup {args.warmup} (nsplit {nsplit})")
+    for _ in range(args.warmup):
+        rc = fa.fa_fwd_splitkv(*call)
+        if rc != 0:
+            raise SystemExit(f"fa_fwd_splitkv failed: {rc} {fa.fa_strerror(rc)}")
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fa.fa_fwd_splitkv(*call)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    gbs = cfg.algorithmic_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] {ms:.4f} ms/step, {gbs:.0f} GB/s ({100 * gbs / 8000:.1f}% of 8000 GB/s)")
+    out = {
+        "metric": "split-K/V decode: algorithmic HBM GB/s (Q, K, V read once; O, lse written once)",
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": gen.DTYPE_NAMES[cfg.dtype],
+        "data": "synthetic (seeded SplitMix64 + Box-Muller normals)",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "Lq": cfg.Lq, "Lk": cfg.Lk, "d": cfg.d,
+                   "scale": cfg.scale, "nsplit": nsplit, "tflops": cfg.flops / (ms * 1e-3) / 1e12},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": 8000.0,
+            "unit": "GB/s",
+            "frac": gbs / 8000.0,
+            "traffic": None,
+            "kernel": "fa_splitkv_kernel + fa_combine_kernel (one fa_fwd_splitkv call)",
+            "algorithmic_bytes_per_launch": cfg.algorithmic_bytes,
+            "avg_launch_ms": ms,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (fp64 oracle on a sample of heads)")
+        out["cpu_baseline"] = cpu_baseline_decode(cfg, q, k, v, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, help="workload index 0..4 (default 3)")
+    ap.add_argument("--workload", default="3",
+                    help="workload index 0..4 (default 3), or 'decode' for the split-K/V decoding shape")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -124,7 +226,9 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
         return
 
-    cfg = gen.config(args.workload)
+    if args.workload == "decode":
+        return bench_decode(args, torch, fa)
+    cfg = gen.config(int(args.workload))
     log(f"[bench] workload {cfg.index}: {cfg.name}; generating inputs")
     q, k, v = gen.make_qkv(cfg)
 

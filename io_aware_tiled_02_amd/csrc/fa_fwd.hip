@@ -17,25 +17,29 @@
 // "FlashAttention 深度解析" (second article, section 2.3).
 //
 // gfx950 mapping
-//  * Each wavefront owns QPW = 32*NQB query rows and does every step for them
-//    alone, so no row statistic is ever combined across waves.
+//  * Each wavefront owns 32 query rows and does every step for them alone, so
+//    no row statistic is ever combined across waves.
 //  * The score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_{bf16,f16}: in the 32x32 accumulator layout a lane
 //    holds ONE query (its column) and 16 keys, so the row max and row sum are
 //    plain in-register max/add chains plus one exchange with lane^32.
 //  * The output is accumulated transposed too, O^T += V^T P^T: the P values a
 //    lane holds are exactly the B operand it needs, so P never leaves
-//    registers.  V is written to LDS transposed (d-major), with the 32-key
-//    sub-tile's key positions permuted so that each lane's 8 keys are one
-//    contiguous 16-byte read.
-//  * K and V^T tiles are double-buffered in LDS; tile j+1 is fetched from HBM
-//    into registers with 16-byte loads while tile j is computed.
+//    registers.
+//  * 16-bit types (fa_fwd_h_kernel): 8 waves, 256 query rows, 128-key tiles.
+//    K and V tiles are double-buffered in LDS and filled by LDS-DMA
+//    (buffer_load ... lds, no register staging); V^T operands come from
+//    row-major V through ds_read_b64_tr_b16.  The two groups of 4 waves run
+//    the MFMA work and the softmax of a tile in alternate phases, so each
+//    SIMD overlaps one wave's MFMAs with the other wave's VALU work.
+//  * fp32 (fa_fwd_f32_kernel): 4 waves, K/V staged through registers into
+//    LDS, V written transposed with the 32-key sub-tile's key positions
+//    permuted so each lane's 8 keys are one contiguous 16-byte read;
+//    v_mfma_f32_32x32x2f32 and P kept in fp32.
 //  * 16-byte LDS chunks are XOR-swizzled by row to spread banks.
 //  * Workgroups are renumbered so that every query tile of a head runs on the
 //    same XCD (they share that head's K/V in the XCD's L2); causal tiles are
 //    issued heaviest first.
-//  * The fp32 type uses the same data path with v_mfma_f32_32x32x2f32 and
-//    keeps P in fp32.
 
 #include <hip/hip_runtime.h>
 
