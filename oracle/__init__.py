@@ -9,6 +9,7 @@ Contents
   * ``fwd``   -- the plain definition (materialised score row, safe softmax,
                  weighted sum, logsumexp) in C, float64, OpenMP over rows.
   * ``brute`` -- a separate C brute-force twin for tiny shapes.
+  * ``bwd``   -- gradients dQ, dK, dV for an upstream dO (definition, fp64).
   * ``attn_range`` / ``merge`` -- one K/V block's attention for a few query
                  rows (rectangular, no mask) and the merge of such partial
                  results: the Flash-Decoding task and its combine step.
@@ -58,6 +59,8 @@ def _load():
         lib.fa_oracle_range.restype = i
         lib.fa_oracle_merge.argtypes = [vp, vp, i, i, i, vp, vp]
         lib.fa_oracle_merge.restype = i
+        lib.fa_oracle_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, d, i, vp, vp, vp, i]
+        lib.fa_oracle_bwd.restype = i
         lib.fa_oracle_max_threads.argtypes = []
         lib.fa_oracle_max_threads.restype = i
         _lib = lib
@@ -156,3 +159,24 @@ def merge(o_parts, lse_parts):
     if rc != 0:
         raise ValueError(f"fa_oracle_merge rejected its arguments (rc={rc})")
     return o, lse
+
+
+def bwd(q, k, v, dout, dtype: int, scale: float, causal: int, nthreads: int = 0):
+    """dQ, dK, dV (each float64 (B,H,L,d)) of attention for upstream gradient dout."""
+    q = _storage_check(q, dtype)
+    k = _storage_check(k, dtype)
+    v = _storage_check(v, dtype)
+    dout = _storage_check(dout, dtype)
+    B, H, L, d = q.shape
+    for a in (k, v, dout):
+        if a.shape != q.shape:
+            raise ValueError("q, k, v, dout must share one (B, H, L, d) shape")
+    dq = np.empty((B, H, L, d), dtype=np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    rc = _load().fa_oracle_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, dtype,
+                               B, H, L, d, float(scale), int(causal), dq.ctypes.data, dk.ctypes.data,
+                               dv.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"fa_oracle_bwd rejected its arguments (rc={rc})")
+    return dq, dk, dv

@@ -256,3 +256,95 @@ int fa_oracle_merge(const double* o_parts, const double* lse_parts, int nsplit, 
     }
     return 0;
 }
+
+/* ---- gradients (definition in float64, P materialised per head) ---- */
+
+int fa_oracle_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                  int B, int H, int L, int d, double scale, int causal,
+                  double* dq, double* dk, double* dv, int nthreads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16 && dtype != ORACLE_F64)
+        return -1;
+    if (B <= 0 || H <= 0 || L <= 0 || d <= 0) return -1;
+    if (causal != 0 && causal != 1) return -1;
+    if (nthreads <= 0) nthreads = fa_oracle_max_threads();
+    const size_t head = (size_t)L * d;
+    double* qd = (double*)malloc(head * sizeof(double));
+    double* kd = (double*)malloc(head * sizeof(double));
+    double* vd = (double*)malloc(head * sizeof(double));
+    double* gd = (double*)malloc(head * sizeof(double));
+    double* P = (double*)malloc((size_t)L * L * sizeof(double));
+    double* dS = (double*)malloc((size_t)L * L * sizeof(double));
+    if (!qd || !kd || !vd || !gd || !P || !dS) {
+        free(qd); free(kd); free(vd); free(gd); free(P); free(dS);
+        return -1;
+    }
+    for (int bh = 0; bh < B * H; ++bh) {
+        const size_t base = (size_t)bh * head;
+        for (size_t e = 0; e < head; ++e) {
+            qd[e] = widen(q, dtype, base + e);
+            kd[e] = widen(k, dtype, base + e);
+            vd[e] = widen(v, dtype, base + e);
+            gd[e] = widen(dout, dtype, base + e);
+        }
+        /* per query row: P row (softmax of the scaled scores), dP row, dS row */
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 4)
+        for (int i = 0; i < L; ++i) {
+            double* p = P + (size_t)i * L;
+            double* ds = dS + (size_t)i * L;
+            double m = -INFINITY;
+            for (int j = 0; j < L; ++j) {
+                if (causal && j > i) {
+                    p[j] = -INFINITY;
+                    continue;
+                }
+                double dot = 0.0;
+                for (int c = 0; c < d; ++c) dot += qd[(size_t)i * d + c] * kd[(size_t)j * d + c];
+                p[j] = scale * dot;
+                if (p[j] > m) m = p[j];
+            }
+            double l = 0.0;
+            for (int j = 0; j < L; ++j) {
+                p[j] = exp(p[j] - m);
+                l += p[j];
+            }
+            for (int j = 0; j < L; ++j) p[j] /= l;
+            /* dP_ij = dO_i . V_j, and the row sum of dP (.) P */
+            double rs = 0.0;
+            for (int j = 0; j < L; ++j) {
+                double dot = 0.0;
+                for (int c = 0; c < d; ++c) dot += gd[(size_t)i * d + c] * vd[(size_t)j * d + c];
+                ds[j] = dot;
+                rs += dot * p[j];
+            }
+            for (int j = 0; j < L; ++j) ds[j] = p[j] * (ds[j] - rs);
+            /* dQ_i = scale * sum_j dS_ij K_j */
+            double* gq = dq + base + (size_t)i * d;
+            for (int c = 0; c < d; ++c) gq[c] = 0.0;
+            for (int j = 0; j < L; ++j)
+                for (int c = 0; c < d; ++c) gq[c] += ds[j] * kd[(size_t)j * d + c];
+            for (int c = 0; c < d; ++c) gq[c] *= scale;
+        }
+        /* per key row: dV_j = sum_i P_ij dO_i, dK_j = scale * sum_i dS_ij Q_i */
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 4)
+        for (int j = 0; j < L; ++j) {
+            double* gv = dv + base + (size_t)j * d;
+            double* gk = dk + base + (size_t)j * d;
+            for (int c = 0; c < d; ++c) {
+                gv[c] = 0.0;
+                gk[c] = 0.0;
+            }
+            for (int i = 0; i < L; ++i) {
+                const double pij = P[(size_t)i * L + j];
+                const double sij = dS[(size_t)i * L + j];
+                for (int c = 0; c < d; ++c) {
+                    gv[c] += pij * gd[(size_t)i * d + c];
+                    gk[c] += sij * qd[(size_t)i * d + c];
+                }
+            }
+            for (int c = 0; c < d; ++c) gk[c] *= scale;
+        }
+    }
+    free(qd); free(kd); free(vd); free(gd); free(P); free(dS);
+    return 0;
+}

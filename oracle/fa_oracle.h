@@ -88,6 +88,24 @@ int fa_oracle_range(const void* q, const void* k, const void* v, int dtype,
 int fa_oracle_merge(const double* o_parts, const double* lse_parts, int nsplit, int n, int d,
                     double* o, double* lse);
 
+/*
+ * Gradients of attention with respect to q, k and v for an upstream gradient
+ * dO of the output ("FlashAttention 深度解析", first article, section 4.1):
+ *     P   = softmax_rows(S),   S = scale * Q K^T (causal: key j > query i is -inf)
+ *     dV  = P^T dO
+ *     dP  = dO V^T
+ *     dS  = dP (.) P - P (.) (sum_j dP_ij P_ij)      (row-wise sum)
+ *     dQ  = scale * dS K,      dK = scale * dS^T Q
+ * (dQ and dK are the chain rule through S = scale * Q K^T.)  P is formed here
+ * from the definition in float64; the GPU recomputes it from the stored lse.
+ * q, k, v, dout : host (B, H, L, d) in the storage type `dtype`.
+ * dq, dk, dv    : host float64 (B, H, L, d).  Returns 0, or -1 on a bad
+ * argument (nothing written).  Cost O(L^2 d) per head, OpenMP over rows.
+ */
+int fa_oracle_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                  int B, int H, int L, int d, double scale, int causal,
+                  double* dq, double* dk, double* dv, int nthreads);
+
 /* Threads an fa_oracle_fwd call with nthreads <= 0 would use. */
 int fa_oracle_max_threads(void);
 
