@@ -29,7 +29,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from .configs import CONFIGS, DECODE, Config, DecodeConfig, config  # noqa: F401
+from .configs import BWD, CONFIGS, DECODE, BwdConfig, Config, DecodeConfig, config  # noqa: F401
 
 F32, F16, BF16 = 0, 1, 2
 DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
@@ -183,3 +183,9 @@ def make_decode_qkv(cfg):
     k = fill(cfg.dtype, (cfg.B, cfg.H, cfg.Lk, cfg.d), cfg.seed, 1, cfg.sigma_k)
     v = fill(cfg.dtype, (cfg.B, cfg.H, cfg.Lk, cfg.d), cfg.seed, 2, cfg.sigma_v)
     return q, k, v
+
+
+def make_bwd_inputs(cfg):
+    """Q, K, V and dO storage arrays (B, H, L, d) for a backward shape."""
+    shape = (cfg.B, cfg.H, cfg.L, cfg.d)
+    return tuple(fill(cfg.dtype, shape, cfg.seed, s) for s in range(4))

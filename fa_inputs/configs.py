@@ -96,3 +96,31 @@ class DecodeConfig:
 # of K/V in bf16.  Seed 10; streams 0/1/2 are Q/K/V.
 DECODE = DecodeConfig("decode bf16 B8 H32 Lq1 Lk16384 d128", 8, 32, 1, 16384, 128, 2,
                       1.0 / math.sqrt(128.0), 10)
+
+
+@dataclass(frozen=True)
+class BwdConfig:
+    """A backward-pass shape: Q, K, V and the upstream gradient dO, (B, H, L, d)."""
+    name: str
+    B: int
+    H: int
+    L: int
+    d: int
+    dtype: int
+    causal: int
+    scale: float
+    seed: int
+
+    @property
+    def flops(self) -> int:
+        """10*B*H*L^2*d: the five L x L x d products of the backward pass
+        (S, dP, dV, dK, dQ), halved when causal."""
+        f = 10 * self.B * self.H * self.L * self.L * self.d
+        return f // 2 if self.causal else f
+
+
+# Backward shapes.  Seeds 20/21; streams 0/1/2/3 are Q/K/V/dO.
+BWD = [
+    BwdConfig("bwd bf16 B1 H32 L8192 d128", 1, 32, 8192, 128, 2, 0, 1.0 / math.sqrt(128.0), 20),
+    BwdConfig("bwd bf16 causal B2 H32 L4096 d128", 2, 32, 4096, 128, 2, 1, 1.0 / math.sqrt(128.0), 21),
+]

@@ -167,6 +167,42 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 int fa_combine(const float* o_part, const float* lse_part, int nsplit, int B, int H, int Lq, int d,
                void* o, float* lse, int dtype, hipStream_t stream);
 
+/*
+ * ---- Backward pass (gradients with respect to q, k, v) ----
+ *
+ * For an upstream gradient dO of the output of fa_fwd ("FlashAttention
+ * 深度解析", first article, section 4.1: dV = P^T dO, dP = dO V^T,
+ * dS = dP (.) P - P (.) rowsum(dP (.) P); dQ = scale dS K and dK = scale dS^T Q
+ * by the chain rule through S = scale Q K^T), with P recomputed from q, k and
+ * the lse of the forward pass rather than stored ("Recomputation": "04
+ * Transformers, Attention, and FlashAttention").  rowsum(dP (.) P)_i is taken
+ * as dO_i . O_i, which equals it because O_i = sum_j P_ij V_j.
+ */
+
+/* fa_bwd_workspace_bytes -- device workspace fa_bwd needs (B*H*L floats,
+ * rounded up to 256 bytes); 0 for non-positive sizes. */
+size_t fa_bwd_workspace_bytes(int B, int H, int L);
+
+/*
+ * fa_bwd -- enqueue the backward pass on `stream`.
+ *
+ * q, k, v : the forward pass's inputs; o, lse : its outputs (o in the storage
+ *           type, lse float32 (B, H, L)); dout : dO, (B, H, L, d).  All read only.
+ * dq, dk, dv : device, (B, H, L, d) in the storage type; fully overwritten
+ *           (fp32 accumulation, one rounding at the end).
+ * Layouts, B, H, L, d, scale and causal as for fa_fwd; dtype FA_F16 or
+ * FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED).
+ * workspace, workspace_size : caller-owned device scratch of at least
+ *           fa_bwd_workspace_bytes(B, H, L) bytes, 256-byte aligned; it holds
+ *           D = rowsum(dO (.) O) until the kernels on `stream` have read it.
+ * Ownership, asynchrony and errors as for fa_fwd (all tensors 16-byte
+ * aligned, lse 4-byte aligned); B*H > 65535 or L*d*2 >= 2^31 returns
+ * FA_ERR_INVALID_ARG.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, int B, int H, int L, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_size, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,10 @@ def load():
         lib.fa_fwd_splitkv.restype = i
         lib.fa_combine.argtypes = [vp, vp, i, i, i, i, i, vp, vp, i, vp]
         lib.fa_combine.restype = i
+        lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+        lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+        lib.fa_bwd.restype = i
         _lib = lib
     return _lib
 
@@ -76,6 +80,17 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, works
 def fa_combine(o_part, lse_part, nsplit, B, H, Lq, d, o, lse, dtype, stream) -> int:
     """The C entry point as is (raw device addresses and stream handle)."""
     return load().fa_combine(o_part, lse_part, nsplit, B, H, Lq, d, o, lse, dtype, stream)
+
+
+def fa_bwd_workspace_bytes(B, H, L) -> int:
+    return load().fa_bwd_workspace_bytes(B, H, L)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, L, d, scale, causal, dtype, workspace, workspace_size,
+           stream) -> int:
+    """The C entry point as is (raw device addresses and stream handle)."""
+    return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, L, d, scale, causal, dtype, workspace,
+                         workspace_size, stream)
 
 
 def fa_strerror(code: int) -> str:
@@ -163,3 +178,25 @@ def forward_splitkv(q, k, v, scale: float, nsplit: int = 0, out=None, lse=None, 
     if rc != FA_OK:
         raise FAError(rc, fa_strerror(rc))
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, scale: float, causal: bool = False, workspace=None, stream=None):
+    """dq, dk, dv for torch device tensors (B, H, L, d); o, lse from forward()."""
+    import torch
+    for t in (q, k, v, o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v, o, dout must be contiguous device tensors of one shape and dtype")
+    B, H, L, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = fa_bwd_workspace_bytes(B, H, L)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d, float(scale), int(bool(causal)),
+                _dtype_code(q), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                stream.cuda_stream)
+    if rc != FA_OK:
+        raise FAError(rc, fa_strerror(rc))
+    return dq, dk, dv

@@ -1,0 +1,506 @@
+// Backward pass of exact attention for gfx950 (MI355X), 16-bit types.
+//
+// Gradients for an upstream dO ("FlashAttention 深度解析", first article,
+// section 4: dV = P^T dO, dP = dO V^T, dS = dP (.) P - P (.) rowsum(dP (.) P),
+// and the chain rule through S = scale Q K^T for dQ and dK), with P
+// recomputed from Q, K and the logsumexp the forward pass stored instead of
+// being kept ("Recomputation": "04 Transformers, Attention, and
+// FlashAttention" and "FlashAttention: как реально считается attention на
+// GPU", backward pass).  rowsum(dP (.) P)_i equals dO_i . O_i, because
+// O_i = sum_j P_ij V_j; a first kernel computes that vector D from O.
+//
+// gfx950 mapping.  Two kernels do the matrix work, neither needs atomics:
+//  * fa_bwd_dkdv_kernel: one workgroup per 128 keys of a head (4 waves x 32
+//    keys; K and V rows of a wave live in registers as MFMA B operands).  It
+//    streams the head's Q and dO in 64-row tiles through LDS and, per 32x32
+//    block, computes S = Q K^T and dP = dO V^T (lane = key: the accumulator
+//    column), P and dS with each query row's lse and D read from LDS, and
+//    accumulates dV^T += dO^T P and dK^T += Q^T dS, the dO^T and Q^T operands
+//    coming from transposing LDS reads.
+//  * fa_bwd_dq_kernel: one workgroup per 128 queries (4 waves x 32 queries;
+//    Q and dO rows in registers).  It streams K and V in 64-row tiles and
+//    computes S^T = K Q^T and dP^T = V dO^T (lane = query, so lse and D are
+//    one value per lane), dS^T, and dQ^T += K^T dS^T.
+//  So dK/dV and dQ are each reduced inside one workgroup; the price is that
+//  S and dP are formed twice (seven 32x32-tile products per block instead of
+//  five).  Tiles arrive by LDS-DMA into double-buffered stages, rows
+//  XOR-swizzled (the same row layout serves the row reads and the
+//  transposing reads).
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa.h"
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace {
+
+using namespace fa_dev;
+
+struct BwdParams {
+    const char* q;
+    const char* k;
+    const char* v;
+    const char* o;
+    const char* dout;
+    const float* lse;       // (BH, L) natural-log logsumexp from the forward pass
+    float* dvec;            // (BH, L) D_i = dO_i . O_i (workspace)
+    char* dq;
+    char* dk;
+    char* dv;
+    int BH, L;
+    float c;                // scale * log2(e)
+    float scale;
+};
+
+// Streamed tiles: 64 rows of D elements, 16-bit.
+template <int D>
+struct BCfg {
+    static constexpr int P = 2 * D;               // LDS row pitch (bytes)
+    static constexpr int ROWS = 64;
+    static constexpr int TILE = ROWS * P;
+    static constexpr int PPW = TILE / 1024 / 4;   // 1 KB DMA pieces per wave per tile
+    static_assert(PPW * 4 * 1024 == TILE, "tile must split into 1 KB pieces");
+};
+
+// ---- D_i = dO_i . O_i: 16 lanes per row ----
+template <class T, int D>
+__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p, long long rows) {
+    constexpr int E = D / 16;
+    const int lane = threadIdx.x & 63;
+    const long long row = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+    const bool valid = row < rows;
+    float acc = 0.f;
+    if (valid) {
+        float g[E], o[E];
+        const long long off = (row * D + (lane & 15) * E) * 2;
+        load_elems<T, E>(p.dout + off, g);
+        load_elems<T, E>(p.o + off, o);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc = __builtin_fmaf(g[e], o[e], acc);
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    acc += __shfl_xor(acc, 8);
+    if (valid && (lane & 15) == 0) p.dvec[row] = acc;
+}
+
+// Per-lane LDS offsets shared by both kernels.
+//  row[s]      : the 16-byte chunk (2s + hf) of row l32 (A operand of a row
+//                product: lane = row, 8 consecutive d);
+//  trlo/trhi   : transposing reads (A operand d x rows): lane 16g+4e+q reads
+//                row 4*(g>>1) + e (+8 for trhi) of a 16-row step, d columns
+//                of chunk 4dt + 2(g&1) + (q>>1), half (q&1).  Rows 0..15 and
+//                16..31 of a 32-row group share the swizzle (period 16).
+template <int D>
+struct Offs {
+    int row[D / 16];
+    int trlo[D / 32], trhi[D / 32];
+    __device__ void init(int lane) {
+        using Lay = HLayout<D>;
+        constexpr int P = 2 * D;
+        const int l32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) row[s] = l32 * P + (((2 * s + hf) ^ Lay::fk(l32)) << 4);
+        const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+        const int r = 4 * (g >> 1) + e;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int c = 4 * dt + 2 * (g & 1) + (q >> 1);
+            trlo[dt] = r * P + ((c ^ Lay::fk(r)) << 4) + 8 * (q & 1);
+            trhi[dt] = (r + 8) * P + ((c ^ Lay::fk(r + 8)) << 4) + 8 * (q & 1);
+        }
+    }
+};
+
+// DMA: piece n of a tile (1 KB, lane l its 16 bytes at LDS offset 1024n+16l)
+// holds global chunk slot ^ fk(row) of that row.
+template <int D>
+__device__ inline int dma_goff(int n, int lane) {
+    using Lay = HLayout<D>;
+    constexpr int P = 2 * D;
+    const int o = 1024 * n + 16 * lane;
+    const int r = o / P, slot = (o % P) >> 4;
+    return r * P + ((slot ^ Lay::fk(r)) << 4);
+}
+
+// A operand read transposed from a row-major tile at row offset rowb (bytes).
+template <class T>
+__device__ inline typename Ty<T>::frag tr_frag(const lds_char* base, int lo, int hi) {
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + lo));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + hi));
+    return __builtin_bit_cast(typename Ty<T>::frag, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Row fragments (lane = row l32 of `rows`, d elements 16s + 8hf .. +7) from
+// global memory; zero for rows >= L.
+template <class T, int D>
+__device__ inline void load_row_frags(const char* base, int row, int L, int hf, typename Ty<T>::frag* f) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        u32x4 raw = u32x4{0, 0, 0, 0};
+        if (row < L) raw = ld16(base + ((long long)row * D + 16 * s + 8 * hf) * 2);
+        f[s] = __builtin_bit_cast(typename Ty<T>::frag, raw);
+    }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(f[s]));
+}
+
+// ---- dQ: one workgroup per 128 queries ----
+template <class T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void fa_bwd_dq_kernel(BwdParams p) {
+    using Cf = BCfg<D>;
+    using frag = typename Ty<T>::frag;
+    constexpr int P = Cf::P, TILE = Cf::TILE, PPW = Cf::PPW;
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];   // K0 K1 V0 V1
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+    const int L = p.L;
+    const int bh = blockIdx.y;
+    // causal: the last query blocks see the most keys; dispatch them first
+    const int qb = CAUSAL ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int q0 = qb * 128;
+    const int qw = q0 + 32 * wave;
+    const int qend = min(q0 + 128, L);
+    const int ntiles = CAUSAL ? (qend + 63) / 64 : (L + 63) / 64;
+    const int ntw = qw >= L ? 0 : (CAUSAL ? (min(qw + 32, L) + 63) / 64 : ntiles);
+    const long long head = (long long)bh * L * D;
+    const char* kh = p.k + head * 2;
+    const char* vh = p.v + head * 2;
+
+    const int query = qw + l32;
+    frag qf[D / 16], gf[D / 16];
+    load_row_frags<T, D>(p.q + head * 2, query, L, hf, qf);
+    load_row_frags<T, D>(p.dout + head * 2, query, L, hf, gf);
+    const float lse2 = query < L ? p.lse[(long long)bh * L + query] * kLog2e : 0.f;
+    const float dval = query < L ? p.dvec[(long long)bh * L + query] : 0.f;
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+
+    Offs<D> off;
+    off.init(lane);
+    int goff[PPW];
+#pragma unroll
+    for (int x = 0; x < PPW; ++x) goff[x] = dma_goff<D>(wave * PPW + x, lane);
+    const unsigned lds0 = (unsigned)(unsigned long long)(lds_char*)smem;
+    auto dma_tile = [&](int t) {                  // K_t, V_t into stage t & 1
+        const i32x4 kr = buffer_rsrc_at(kh, L * P, t * TILE);
+        const i32x4 vr = buffer_rsrc_at(vh, L * P, t * TILE);
+#pragma unroll
+        for (int x = 0; x < PPW; ++x) {
+            const unsigned dst = lds0 + (t & 1) * TILE + 1024 * (wave * PPW + x);
+            dma16(kr, goff[x], __builtin_amdgcn_readfirstlane(dst));
+            dma16(vr, goff[x], __builtin_amdgcn_readfirstlane(dst + 2 * TILE));
+        }
+    };
+
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    auto compute = [&](auto mask_tag, int t) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const char* ks = smem + (t & 1) * TILE;
+        const char* vs = smem + 2 * TILE + (t & 1) * TILE;
+        const lds_char* ksl = (const lds_char*)smem + (t & 1) * TILE;
+        const int last = CAUSAL ? min(query, L - 1) : L - 1;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x16 st, dpt;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[r] = dpt[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) {
+                const frag a = __builtin_bit_cast(frag, ld16(ks + kt * 32 * P + off.row[s]));
+                const frag b = __builtin_bit_cast(frag, ld16(vs + kt * 32 * P + off.row[s]));
+                st = Ty<T>::mma(a, qf[s], st);
+                dpt = Ty<T>::mma(b, gf[s], dpt);
+            }
+            // register r holds key t*64 + 32kt + 4hf + 8(r/4) + r%4
+            const int lim = last - t * 64 - 32 * kt - 4 * hf;
+            float ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], p.c, -lse2));
+                if (MASK && 8 * (r >> 2) + (r & 3) > lim) pr = 0.f;
+                ds[r] = pr * (dpt[r] - dval);
+            }
+            const frag d0 = Ty<T>::cvt(ds), d1 = Ty<T>::cvt(ds + 8);
+#pragma unroll
+            for (int ps = 0; ps < 2; ++ps) {
+                const int rowb = (kt * 32 + 16 * ps) * P;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    const frag a = tr_frag<T>(ksl + rowb, off.trlo[dt], off.trhi[dt]);
+                    acc[dt] = Ty<T>::mma(a, ps ? d1 : d0, acc[dt]);
+                }
+            }
+        }
+    };
+
+    // first tile with keys past this wave's first query or past L
+    const int jmask = CAUSAL ? min(qw / 64, (L - 1) / 64) : (L - 1) / 64;
+    dma_tile(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) dma_tile(t + 1);
+        if (t < ntw) {
+            if (t < jmask) compute(no{}, t);
+            else compute(yes{}, t);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
+    if (query < L) {
+        char* qrow = p.dq + (head + (long long)query * D) * 2;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                T o4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] = (T)(acc[dt][4 * g + e] * p.scale);
+                st8(qrow + (dt * 32 + g * 8 + hf * 4) * 2, __builtin_bit_cast(u32x2, o4));
+            }
+    }
+}
+
+// ---- dK, dV: one workgroup per 128 keys ----
+template <class T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void fa_bwd_dkdv_kernel(BwdParams p) {
+    using Cf = BCfg<D>;
+    using frag = typename Ty<T>::frag;
+    constexpr int P = Cf::P, TILE = Cf::TILE, PPW = Cf::PPW;
+    // Q0 Q1 dO0 dO1, then per stage 64 lse*log2e and 64 D values
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 2 * 512];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+    const int L = p.L;
+    const int bh = blockIdx.y;
+    const int k0 = blockIdx.x * 128;
+    const int kw = k0 + 32 * wave;
+    const int key = kw + l32;
+    const long long head = (long long)bh * L * D;
+    const char* qh = p.q + head * 2;
+    const char* gh = p.dout + head * 2;
+
+    frag kf[D / 16], vf[D / 16];
+    load_row_frags<T, D>(p.k + head * 2, key, L, hf, kf);
+    load_row_frags<T, D>(p.v + head * 2, key, L, hf, vf);
+    f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dka[dt][r] = dva[dt][r] = 0.f;
+
+    Offs<D> off;
+    off.init(lane);
+    int goff[PPW];
+#pragma unroll
+    for (int x = 0; x < PPW; ++x) goff[x] = dma_goff<D>(wave * PPW + x, lane);
+    const unsigned lds0 = (unsigned)(unsigned long long)(lds_char*)smem;
+    float* stats = reinterpret_cast<float*>(smem + 4 * TILE);
+    auto dma_tile = [&](int t) {                  // Q_t, dO_t into stage t & 1
+        const i32x4 qr = buffer_rsrc_at(qh, L * P, t * TILE);
+        const i32x4 gr = buffer_rsrc_at(gh, L * P, t * TILE);
+#pragma unroll
+        for (int x = 0; x < PPW; ++x) {
+            const unsigned dst = lds0 + (t & 1) * TILE + 1024 * (wave * PPW + x);
+            dma16(qr, goff[x], __builtin_amdgcn_readfirstlane(dst));
+            dma16(gr, goff[x], __builtin_amdgcn_readfirstlane(dst + 2 * TILE));
+        }
+    };
+    // row statistics of tile t (wave 0): lse in base-2 units (+inf past L, so
+    // P = 0 there) and D
+    float st_l = 0.f, st_d = 0.f;
+    auto stats_load = [&](int t) {
+        const int row = t * 64 + lane;
+        st_l = row < L ? p.lse[(long long)bh * L + row] * kLog2e : INFINITY;
+        st_d = row < L ? p.dvec[(long long)bh * L + row] : 0.f;
+    };
+    auto stats_store = [&](int t) {
+        stats[(t & 1) * 128 + lane] = st_l;
+        stats[(t & 1) * 128 + 64 + lane] = st_d;
+    };
+
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    // 32 queries (rows 32*qt.. of tile t) against this wave's 32 keys
+    auto compute = [&](auto mask_tag, int t, int qt) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const char* qs = smem + (t & 1) * TILE;
+        const char* gs = smem + 2 * TILE + (t & 1) * TILE;
+        const lds_char* qsl = (const lds_char*)smem + (t & 1) * TILE;
+        const lds_char* gsl = (const lds_char*)smem + 2 * TILE + (t & 1) * TILE;
+        const float* sl = stats + (t & 1) * 128 + 32 * qt;
+        f32x16 st, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = dp[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const frag a = __builtin_bit_cast(frag, ld16(qs + qt * 32 * P + off.row[s]));
+            const frag b = __builtin_bit_cast(frag, ld16(gs + qt * 32 * P + off.row[s]));
+            st = Ty<T>::mma(a, kf[s], st);
+            dp = Ty<T>::mma(b, vf[s], dp);
+        }
+        // register r holds query t*64 + 32qt + 8(r/4) + 4hf + r%4 of key `key`
+        const int first = t * 64 + 32 * qt + 4 * hf;
+        float pr[16], ds[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 l4 = *reinterpret_cast<const float4*>(sl + 8 * g + 4 * hf);
+            const float4 d4 = *reinterpret_cast<const float4*>(sl + 64 + 8 * g + 4 * hf);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], p.c, -lv[e]));
+                if (MASK && key > first + 8 * g + e) x = 0.f;
+                pr[r] = x;
+                ds[r] = x * (dp[r] - dv[e]);
+            }
+        }
+        const frag p0 = Ty<T>::cvt(pr), p1 = Ty<T>::cvt(pr + 8);
+        const frag s0 = Ty<T>::cvt(ds), s1 = Ty<T>::cvt(ds + 8);
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+            const int rowb = (qt * 32 + 16 * ps) * P;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const frag ga = tr_frag<T>(gsl + rowb, off.trlo[dt], off.trhi[dt]);
+                dva[dt] = Ty<T>::mma(ga, ps ? p1 : p0, dva[dt]);
+                const frag qa = tr_frag<T>(qsl + rowb, off.trlo[dt], off.trhi[dt]);
+                dka[dt] = Ty<T>::mma(qa, ps ? s1 : s0, dka[dt]);
+            }
+        }
+    };
+
+    const int nq = (L + 63) / 64;
+    const int t0 = CAUSAL ? k0 / 64 : 0;          // queries before the first key see none of these keys
+    dma_tile(t0);
+    if (wave == 0) {
+        stats_load(t0);
+        stats_store(t0);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int t = t0; t < nq; ++t) {
+        const bool more = t + 1 < nq;
+        if (more) {
+            dma_tile(t + 1);
+            if (wave == 0) stats_load(t + 1);
+        }
+        if (kw < L) {
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                const int qfirst = t * 64 + 32 * qt;
+                if (CAUSAL && qfirst + 31 < kw) continue;        // every query before every key
+                if (CAUSAL && qfirst < kw + 32) compute(yes{}, t, qt);
+                else compute(no{}, t, qt);
+            }
+        }
+        if (more && wave == 0) stats_store(t + 1);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
+    if (key < L) {
+        char* krow = p.dk + (head + (long long)key * D) * 2;
+        char* vrow = p.dv + (head + (long long)key * D) * 2;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                T k4[4], v4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    k4[e] = (T)(dka[dt][4 * g + e] * p.scale);
+                    v4[e] = (T)dva[dt][4 * g + e];
+                }
+                st8(krow + (dt * 32 + g * 8 + hf * 4) * 2, __builtin_bit_cast(u32x2, k4));
+                st8(vrow + (dt * 32 + g * 8 + hf * 4) * 2, __builtin_bit_cast(u32x2, v4));
+            }
+    }
+}
+
+// ---- host side ----
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+template <class T, int D, bool CAUSAL>
+int launch_bwd(const BwdParams& p, hipStream_t stream) {
+    const long long rows = (long long)p.BH * p.L;
+    hipLaunchKernelGGL((fa_bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p, rows);
+    int rc = fa_detail::launch_status();
+    if (rc != FA_OK) return rc;
+    const dim3 grid((unsigned)((p.L + 127) / 128), (unsigned)p.BH);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
+    rc = fa_detail::launch_status();
+    if (rc != FA_OK) return rc;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
+    return fa_detail::launch_status();
+}
+
+template <class T>
+int launch_bwd_t(const BwdParams& p, int d, int causal, hipStream_t stream) {
+    if (d == 64) return causal ? launch_bwd<T, 64, true>(p, stream) : launch_bwd<T, 64, false>(p, stream);
+    return causal ? launch_bwd<T, 128, true>(p, stream) : launch_bwd<T, 128, false>(p, stream);
+}
+
+size_t dvec_bytes(long long rows) { return ((size_t)rows * sizeof(float) + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int L) {
+    if (B <= 0 || H <= 0 || L <= 0) return 0;
+    return dvec_bytes((long long)B * H * L);
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                      void* dq, void* dk, void* dv, int B, int H, int L, int d, float scale, int causal, int dtype,
+                      void* workspace, size_t workspace_size, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || L <= 0) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H > 65535) return FA_ERR_INVALID_ARG;
+    // per-head byte offsets go through 32-bit buffer descriptors
+    if ((long long)L * d * 2 >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(workspace, 256))
+        return FA_ERR_ALIGN;
+    if (workspace_size < dvec_bytes((long long)B * H * L)) return FA_ERR_INVALID_ARG;
+
+    BwdParams p;
+    p.q = static_cast<const char*>(q);
+    p.k = static_cast<const char*>(k);
+    p.v = static_cast<const char*>(v);
+    p.o = static_cast<const char*>(o);
+    p.dout = static_cast<const char*>(dout);
+    p.lse = lse;
+    p.dvec = static_cast<float*>(workspace);
+    p.dq = static_cast<char*>(dq);
+    p.dk = static_cast<char*>(dk);
+    p.dv = static_cast<char*>(dv);
+    p.BH = B * H;
+    p.L = L;
+    p.c = scale * kLog2e;
+    p.scale = scale;
+    return dtype == FA_BF16 ? launch_bwd_t<__bf16>(p, d, causal, stream) : launch_bwd_t<_Float16>(p, d, causal, stream);
+}

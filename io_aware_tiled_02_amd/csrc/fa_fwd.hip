@@ -49,6 +49,7 @@
 #include <type_traits>
 
 #include "fa.h"
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa_detail {
@@ -66,73 +67,7 @@ int launch_status() {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-// ---- per storage type: fragment of 8 k-values per lane, and the MFMA step ----
-template <class T>
-struct Ty;
-
-template <>
-struct Ty<__bf16> {
-    using frag = bf16x8;
-    static constexpr int kBytes = 2;
-    __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ static inline frag cvt(const float* x) {
-        frag r;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
-        return r;
-    }
-};
-
-template <>
-struct Ty<_Float16> {
-    using frag = f16x8;
-    static constexpr int kBytes = 2;
-    __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    __device__ static inline frag cvt(const float* x) {
-        frag r;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = (_Float16)x[e];
-        return r;
-    }
-};
-
-template <>
-struct Ty<float> {
-    using frag = f32x8;
-    static constexpr int kBytes = 4;
-    // eight k=2 steps; element e of every lane's fragment feeds step e, so
-    // both operands see the same k order
-    __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
-        return c;
-    }
-    __device__ static inline frag cvt(const float* x) {
-        frag r;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = x[e];
-        return r;
-    }
-};
-
-// 16-byte global / LDS accesses
-__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ inline void st16(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
-__device__ inline void st8(void* p, u32x2 x) { *reinterpret_cast<u32x2*>(p) = x; }
+using namespace fa_dev;
 
 // Position of key k (0..31) of a 32-key sub-tile inside a transposed V row.
 // The S^T accumulator register r of lane half h holds key 8*(r/4) + 4h + r%4;
@@ -509,66 +444,6 @@ void fa_fwd_f32_kernel(Params p) {
 //    immediates.
 // ===========================================================================
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-template <int D>
-struct HLayout {
-    static constexpr int P = D * 2;       // row pitch in LDS (bytes), unpadded
-    static constexpr int CPR = D / 8;     // 16-byte chunks per row
-    __device__ static inline int fk(int r) { return (CPR == 16 ? r : (r >> 1)) & (CPR - 1); }
-    __device__ static inline int fv(int r) { return 4 * ((CPR == 16 ? r : (r >> 1)) & (CPR / 4 - 1)); }
-};
-
-// buffer descriptor word 3 for CDNA: raw, untyped 32-bit access
-constexpr int kBufWord3 = 0x00020000;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor over [base, base + bytes): reads past the end return 0.
-__device__ inline i32x4 buffer_rsrc(const void* base, int bytes) {
-    const unsigned long long b = (unsigned long long)base;
-    i32x4 r;
-    r[0] = (int)(b & 0xffffffffu);
-    r[1] = (int)(b >> 32);   // stride 0
-    r[2] = bytes;
-    r[3] = kBufWord3;
-    return r;
-}
-
-// The same buffer advanced by `off` bytes (off a multiple of 16): offsets
-// are checked against what is left, so reads past the end still return 0.
-__device__ inline i32x4 buffer_rsrc_at(const char* base, int bytes, int off) {
-    return buffer_rsrc(base + off, max(bytes - off, 0));
-}
-
-// 16 bytes per lane from buffer offset `voff` into LDS at lds_base + 16*lane
-// (buffer_load_dwordx4 ... lds).  Issued as inline asm so that the compiler's
-// wait-count insertion does not make later LDS reads wait for this DMA: the
-// kernel waits for it explicitly (vmcnt) before the barrier that publishes the
-// tile.  M0 carries the LDS address and is restored afterwards.
-__device__ inline void dma16(i32x4 rsrc, int voff, unsigned lds_base) {
-    int saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_base), "v"(voff), "s"(rsrc)
-        : "memory");
-}
-
-// Exchange with lane^32 (v_permlane32_swap): returns the pair {x, x of lane^32}.
-__device__ inline float pair_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float pair_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 #ifndef FA_H_NKB128
 #define FA_H_NKB128 4

@@ -32,76 +32,14 @@
 #include <stdint.h>
 
 #include "fa.h"
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
+using namespace fa_dev;
+
 constexpr int kMaxLq = 8;
-
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// E consecutive elements of a row, widened to fp32 (E = 4 or 8).
-template <class T, int E>
-__device__ inline void load_elems(const char* p, float* out);
-
-template <>
-__device__ inline void load_elems<__bf16, 8>(const char* p, float* out) {
-    const u32x4 r = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        out[2 * j] = __uint_as_float(r[j] << 16);
-        out[2 * j + 1] = __uint_as_float(r[j] & 0xffff0000u);
-    }
-}
-template <>
-__device__ inline void load_elems<__bf16, 4>(const char* p, float* out) {
-    const u32x2 r = *reinterpret_cast<const u32x2*>(p);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        out[2 * j] = __uint_as_float(r[j] << 16);
-        out[2 * j + 1] = __uint_as_float(r[j] & 0xffff0000u);
-    }
-}
-// The two binary16 halves of a 32-bit word.  (Scalar bit casts: a bit cast
-// of a vector element to a two-half vector was compiled into a load of only
-// the first word.)
-__device__ inline void halves(unsigned w, float* out) {
-    out[0] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
-    out[1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
-}
-template <>
-__device__ inline void load_elems<_Float16, 8>(const char* p, float* out) {
-    const u32x4 r = *reinterpret_cast<const u32x4*>(p);
-    halves(r[0], out);
-    halves(r[1], out + 2);
-    halves(r[2], out + 4);
-    halves(r[3], out + 6);
-}
-template <>
-__device__ inline void load_elems<_Float16, 4>(const char* p, float* out) {
-    const u32x2 r = *reinterpret_cast<const u32x2*>(p);
-    halves(r[0], out);
-    halves(r[1], out + 2);
-}
-template <>
-__device__ inline void load_elems<float, 8>(const char* p, float* out) {
-    const u32x4 a = reinterpret_cast<const u32x4*>(p)[0];
-    const u32x4 b = reinterpret_cast<const u32x4*>(p)[1];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        out[j] = __uint_as_float(a[j]);
-        out[4 + j] = __uint_as_float(b[j]);
-    }
-}
-template <>
-__device__ inline void load_elems<float, 4>(const char* p, float* out) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = __uint_as_float(a[j]);
-}
 
 struct SkParams {
     const char* q;      // (BH, Lq, D)

@@ -126,3 +126,38 @@ def test_splitkv_workspace_size_and_auto_splits():
 ])
 def test_combine_argument_errors(args, want):
     assert fa.fa_combine(*args) == want
+
+
+# ---- backward entry point ------------------------------------------------------
+
+def _bw(**kw):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, B=1, H=2, L=100, d=128, scale=0.1, causal=0,
+             dtype=2, ws=W, wsz=BIG, stream=0)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["B"], a["H"],
+                     a["L"], a["d"], a["scale"], a["causal"], a["dtype"], a["ws"], a["wsz"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(do=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=0), fa.FA_ERR_INVALID_ARG),
+    (dict(L=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED),     # no fp32 backward
+    (dict(B=300, H=300), fa.FA_ERR_INVALID_ARG),
+    (dict(L=1 << 23), fa.FA_ERR_INVALID_ARG),   # L*d*2 >= 2^31
+    (dict(dq=A + 8), fa.FA_ERR_ALIGN),
+    (dict(lse=A + 2), fa.FA_ERR_ALIGN),
+    (dict(ws=W + 64), fa.FA_ERR_ALIGN),
+    (dict(wsz=255), fa.FA_ERR_INVALID_ARG),
+])
+def test_bwd_argument_errors(kw, want):
+    assert _bw(**kw) == want
+
+
+def test_bwd_workspace_size():
+    assert fa.fa_bwd_workspace_bytes(1, 2, 100) == 1024      # 200 floats -> 800 B -> 1024
+    assert fa.fa_bwd_workspace_bytes(0, 2, 100) == 0
