@@ -191,13 +191,118 @@ def bench_decode(args, torch, fa):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_bwd(cfg, q, k, v, g, target_s: float):
+    """The fp64 oracle's gradients for whole heads of the same workload (bounded sample)."""
+    import oracle
+    nth = oracle.max_threads()
+    bh = cfg.B * cfg.H
+    sl = lambda a, n: a.reshape(bh, cfg.L, cfg.d)[:n][None]
+    t = time.perf_counter()
+    oracle.bwd(sl(q, 1), sl(k, 1), sl(v, 1), sl(g, 1), cfg.dtype, cfg.scale, cfg.causal)
+    dt = time.perf_counter() - t
+    nh = 1
+    if dt < target_s / 2:
+        nh = int(min(bh, max(1, target_s / dt)))
+        t = time.perf_counter()
+        oracle.bwd(sl(q, nh), sl(k, nh), sl(v, nh), sl(g, nh), cfg.dtype, cfg.scale, cfg.causal)
+        dt = time.perf_counter() - t
+    flops = cfg.flops * nh / bh
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": nth,
+        "kind": "oracle",
+        "sample": f"{nh} of {bh} heads of the same workload (every row), fp64 C oracle, OpenMP; {dt:.1f} s",
+        "seconds": dt,
+        "cpu_model": _cpu_model(),
+        "nproc": os.cpu_count(),
+    }
+
+
+def bench_bwd(args, torch, fa, cfg):
+    """The backward pass (fa_bwd: D, dK/dV, dQ kernels) after one forward pass for o and lse."""
+    log(f"[bench] backward: {cfg.name}; generating inputs")
+    q, k, v, g = gen.make_bwd_inputs(cfg)
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    qd, kd, vd, gd = (dev(x) for x in (q, k, v, g))
+    B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    rc = fa.fa_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, L, d,
+                   float(cfg.scale), cfg.causal, cfg.dtype, stream.cuda_stream)
+    if rc != 0:
+        raise SystemExit(f"fa_fwd failed: {rc} {fa.fa_strerror(rc)}")
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    need = fa.fa_bwd_workspace_bytes(B, H, L)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    call = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), gd.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, L, d, float(cfg.scale), cfg.causal, cfg.dtype,
+            ws.data_ptr(), need, stream.cuda_stream)
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        rc = fa.fa_bwd(*call)
+        if rc != 0:
+            raise SystemExit(f"fa_bwd failed: {rc} {fa.fa_strerror(rc)}")
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fa.fa_bwd(*call)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = cfg.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    log(f"[bench] {ms:.4f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak})")
+    out = {
+        "metric": "attention bwd TFLOP/s (10*B*H*L^2*d: S, dP, dV, dK, dQ products; half for causal) "
+                  "and % of MI355X bf16 MFMA peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": gen.DTYPE_NAMES[cfg.dtype],
+        "data": "synthetic (seeded SplitMix64 + Box-Muller normals)",
+        "config": {"workload": cfg.name, "B": B, "H": H, "L": L, "d": d, "causal": bool(cfg.causal),
+                   "scale": cfg.scale, "pct_of_peak": 100.0 * tflops / peak},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": tflops / peak,
+            "traffic": None,
+            "kernel": "fa_bwd_pre_kernel + fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (one fa_bwd call)",
+            "per_launch_flops": cfg.flops,
+            "avg_launch_ms": ms,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (fp64 oracle gradients on whole heads)")
+        out["cpu_baseline"] = cpu_baseline_bwd(cfg, q, k, v, g, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="3",
-                    help="workload index 0..4 (default 3), or 'decode' for the split-K/V decoding shape")
+                    help="workload index 0..4 (default 3); 'decode' (split-K/V decoding shape); "
+                         "'bwd' / 'bwd-causal' (backward pass shapes)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -228,6 +333,8 @@ def main():
 
     if args.workload == "decode":
         return bench_decode(args, torch, fa)
+    if args.workload in ("bwd", "bwd-causal"):
+        return bench_bwd(args, torch, fa, gen.BWD[0 if args.workload == "bwd" else 1])
     cfg = gen.config(int(args.workload))
     log(f"[bench] workload {cfg.index}: {cfg.name}; generating inputs")
     q, k, v = gen.make_qkv(cfg)
