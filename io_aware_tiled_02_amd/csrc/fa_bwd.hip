@@ -154,7 +154,8 @@ __device__ inline void load_row_frags(const char* base, int row, int L, int hf, 
 
 // ---- dQ: one workgroup per 128 queries ----
 template <class T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void fa_bwd_dq_kernel(BwdParams p) {
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dq_kernel(BwdParams p) {
     using Cf = BCfg<D>;
     using frag = typename Ty<T>::frag;
     constexpr int P = Cf::P, TILE = Cf::TILE, PPW = Cf::PPW;
@@ -247,20 +248,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void fa_bwd_dq
         }
     };
 
-    // first tile with keys past this wave's first query or past L
+    // first tile with keys past this wave's first query or past L; the
+    // tiles before it and from it on run in separate loops, so that only one
+    // variant of the tile code is live at a time (register budget)
     const int jmask = CAUSAL ? min(qw / 64, (L - 1) / 64) : (L - 1) / 64;
+    const int jm = min(jmask, ntiles);
+    auto step = [&](auto mask_tag, int t) {
+        if (t + 1 < ntiles) dma_tile(t + 1);
+        if (t < ntw) compute(mask_tag, t);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
     dma_tile(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) dma_tile(t + 1);
-        if (t < ntw) {
-            if (t < jmask) compute(no{}, t);
-            else compute(yes{}, t);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
+    int t = 0;
+    for (; t < jm; ++t) step(no{}, t);
+    for (; t < ntiles; ++t) step(yes{}, t);
 
     if (query < L) {
         char* qrow = p.dq + (head + (long long)query * D) * 2;
@@ -278,7 +282,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void fa_bwd_dq
 
 // ---- dK, dV: one workgroup per 128 keys ----
 template <class T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void fa_bwd_dkdv_kernel(BwdParams p) {
+__device__ __attribute__((always_inline)) inline void fa_bwd_dkdv_body(const BwdParams& p) {
     using Cf = BCfg<D>;
     using frag = typename Ty<T>::frag;
     constexpr int P = Cf::P, TILE = Cf::TILE, PPW = Cf::PPW;
@@ -398,7 +402,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void fa_bwd_dk
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int t = t0; t < nq; ++t) {
+    // causal: the tiles holding the block's diagonal (queries before k0 + 128)
+    // need the mask; the rest do not.  Separate loops keep one variant of the
+    // tile code live at a time (register budget).
+    auto step = [&](auto mask_tag, int t) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const bool more = t + 1 < nq;
         if (more) {
             dma_tile(t + 1);
@@ -407,16 +415,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void fa_bwd_dk
         if (kw < L) {
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
-                const int qfirst = t * 64 + 32 * qt;
-                if (CAUSAL && qfirst + 31 < kw) continue;        // every query before every key
-                if (CAUSAL && qfirst < kw + 32) compute(yes{}, t, qt);
-                else compute(no{}, t, qt);
+                // every query before every key of this wave: nothing to add
+                if (MASK && t * 64 + 32 * qt + 31 < kw) continue;
+                compute(mask_tag, t, qt);
             }
         }
         if (more && wave == 0) stats_store(t + 1);
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
-    }
+    };
+    const int tdiag = CAUSAL ? min(nq, (k0 + 128 + 63) / 64) : t0;
+    int t = t0;
+    for (; t < tdiag; ++t) step(yes{}, t);
+    for (; t < nq; ++t) step(no{}, t);
 
     if (key < L) {
         char* krow = p.dk + (head + (long long)key * D) * 2;
@@ -437,6 +448,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void fa_bwd_dk
     }
 }
 
+// Two waves per SIMD where the registers allow it (non-causal); the causal
+// variant's masked diagonal tiles need more registers than that leaves.
+template <class T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkdv_kernel(BwdParams p) {
+    fa_bwd_dkdv_body<T, D, CAUSAL>(p);
+}
+template <class T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkdv1_kernel(BwdParams p) {
+    fa_bwd_dkdv_body<T, D, CAUSAL>(p);
+}
+
 // ---- host side ----
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -451,7 +475,10 @@ int launch_bwd(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
     rc = fa_detail::launch_status();
     if (rc != FA_OK) return rc;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
+    if constexpr (CAUSAL)
+        hipLaunchKernelGGL((fa_bwd_dkdv1_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
     return fa_detail::launch_status();
 }
 
