@@ -27,7 +27,8 @@ import fa_inputs as gen  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s (4·B·H·L²·d) and % of MI355X bf16 MFMA peak"
 PEAK_TFLOPS = {gen.BF16: 2516.6, gen.F16: 2516.6, gen.F32: 157.3}   # dense MFMA peaks, MI355X
-KERNEL_SRC = os.path.join(ROOT, "io_aware_tiled_02_amd", "csrc", "fa_fwd.hip")
+# the sources the forward kernel is compiled from (the traffic record is keyed to them)
+KERNEL_SRCS = [os.path.join(ROOT, "io_aware_tiled_02_amd", "csrc", n) for n in ("fa_fwd.hip", "fa_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_kernel.json")
 
 
@@ -36,7 +37,10 @@ def log(msg):
 
 
 def kernel_digest() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
 
 
 def traffic_for(workload_index: int):
