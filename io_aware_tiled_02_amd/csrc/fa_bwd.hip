@@ -91,36 +91,48 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p, long long 
     if (valid && (lane & 15) == 0) p.dvec[row] = acc;
 }
 
-// Per-lane LDS offsets shared by both kernels.
-//  row[s]      : the 16-byte chunk (2s + hf) of row l32 (A operand of a row
-//                product: lane = row, 8 consecutive d);
-//  trlo/trhi   : transposing reads (A operand d x rows): lane 16g+4e+q reads
-//                row 4*(g>>1) + e (+8 for trhi) of a 16-row step, d columns
-//                of chunk 4dt + 2(g&1) + (q>>1), half (q&1).  Rows 0..15 and
-//                16..31 of a 32-row group share the swizzle (period 16).
+// Per-lane LDS offsets shared by both kernels, all derived from two base
+// values by XOR with constants (so only the bases stay live across a loop).
+//  row(s)    : the 16-byte chunk (2s + hf) of row l32 (A operand of a row
+//              product: lane = row, 8 consecutive d).  That chunk sits at
+//              (2s + hf) ^ fk(l32); s only enters the bits above bit 0 of the
+//              chunk index, so row(s) = row(0) ^ (s << 5).
+//  tr(dt,hi) : transposing reads (A operand d x rows): lane 16g+4e+q reads
+//              row 4*(g>>1) + e (+8 for hi) of a 16-row step, d columns of
+//              chunk 4dt + 2(g&1) + (q>>1), half (q&1).  dt flips chunk bits
+//              2.. (offset bits 6..); the +8 rows flip one row bit and the
+//              swizzle bit it drives.  Rows 0..15 and 16..31 of a 32-row
+//              group share the swizzle (period 16).
 template <int D>
 struct Offs {
-    int row[D / 16];
-    int trlo[D / 32], trhi[D / 32];
+    static constexpr int kTrHi = D == 128 ? 0x880 : 0x440;
+    int row0, tr0;
+    __device__ int row(int s) const { return row0 ^ (s << 5); }
+    __device__ int tr(int dt, int hi) const { return tr0 ^ (dt << 6) ^ (hi ? kTrHi : 0); }
     __device__ void init(int lane) {
         using Lay = HLayout<D>;
         constexpr int P = 2 * D;
         const int l32 = lane & 31, hf = lane >> 5;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) row[s] = l32 * P + (((2 * s + hf) ^ Lay::fk(l32)) << 4);
+        row0 = l32 * P + ((hf ^ Lay::fk(l32)) << 4);
         const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
         const int r = 4 * (g >> 1) + e;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            const int c = 4 * dt + 2 * (g & 1) + (q >> 1);
-            trlo[dt] = r * P + ((c ^ Lay::fk(r)) << 4) + 8 * (q & 1);
-            trhi[dt] = (r + 8) * P + ((c ^ Lay::fk(r + 8)) << 4) + 8 * (q & 1);
-        }
+        const int c = 2 * (g & 1) + (q >> 1);
+        tr0 = r * P + ((c ^ Lay::fk(r)) << 4) + 8 * (q & 1);
+    }
+    // The same offsets, opaque to the optimiser: called inside a loop body, the
+    // derived offsets are recomputed there (a few XORs) instead of being
+    // hoisted and kept live, or spilled, across the loop.
+    __device__ Offs fresh() const {
+        Offs o = *this;
+        asm volatile("" : "+v"(o.row0), "+v"(o.tr0));
+        return o;
     }
 };
 
 // DMA: piece n of a tile (1 KB, lane l its 16 bytes at LDS offset 1024n+16l)
-// holds global chunk slot ^ fk(row) of that row.
+// holds global chunk slot ^ fk(row) of that row.  For the PPW pieces of one
+// wave, piece wave*PPW + x reads at dma_goff(wave*PPW) ^ (x * 0x440): x adds
+// 4 rows (bit 10) and flips swizzle bit 2 of the chunk (bit 6).
 template <int D>
 __device__ inline int dma_goff(int n, int lane) {
     using Lay = HLayout<D>;
@@ -191,18 +203,18 @@ void fa_bwd_dq_kernel(BwdParams p) {
 
     Offs<D> off;
     off.init(lane);
-    int goff[PPW];
-#pragma unroll
-    for (int x = 0; x < PPW; ++x) goff[x] = dma_goff<D>(wave * PPW + x, lane);
+    const int goff0 = dma_goff<D>(wave * PPW, lane);
     const unsigned lds0 = (unsigned)(unsigned long long)(lds_char*)smem;
     auto dma_tile = [&](int t) {                  // K_t, V_t into stage t & 1
         const i32x4 kr = buffer_rsrc_at(kh, L * P, t * TILE);
         const i32x4 vr = buffer_rsrc_at(vh, L * P, t * TILE);
+        int g0 = goff0;
+        asm volatile("" : "+v"(g0));              // derive the piece offsets here, not across the loop
 #pragma unroll
         for (int x = 0; x < PPW; ++x) {
             const unsigned dst = lds0 + (t & 1) * TILE + 1024 * (wave * PPW + x);
-            dma16(kr, goff[x], __builtin_amdgcn_readfirstlane(dst));
-            dma16(vr, goff[x], __builtin_amdgcn_readfirstlane(dst + 2 * TILE));
+            dma16(kr, g0 ^ (x * 0x440), __builtin_amdgcn_readfirstlane(dst));
+            dma16(vr, g0 ^ (x * 0x440), __builtin_amdgcn_readfirstlane(dst + 2 * TILE));
         }
     };
 
@@ -213,6 +225,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
         const char* ks = smem + (t & 1) * TILE;
         const char* vs = smem + 2 * TILE + (t & 1) * TILE;
         const lds_char* ksl = (const lds_char*)smem + (t & 1) * TILE;
+        const Offs<D> o = off.fresh();
         const int last = CAUSAL ? min(query, L - 1) : L - 1;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
@@ -221,8 +234,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
             for (int r = 0; r < 16; ++r) st[r] = dpt[r] = 0.f;
 #pragma unroll
             for (int s = 0; s < D / 16; ++s) {
-                const frag a = __builtin_bit_cast(frag, ld16(ks + kt * 32 * P + off.row[s]));
-                const frag b = __builtin_bit_cast(frag, ld16(vs + kt * 32 * P + off.row[s]));
+                const frag a = __builtin_bit_cast(frag, ld16(ks + kt * 32 * P + o.row(s)));
+                const frag b = __builtin_bit_cast(frag, ld16(vs + kt * 32 * P + o.row(s)));
                 st = Ty<T>::mma(a, qf[s], st);
                 dpt = Ty<T>::mma(b, gf[s], dpt);
             }
@@ -241,7 +254,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
                 const int rowb = (kt * 32 + 16 * ps) * P;
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
-                    const frag a = tr_frag<T>(ksl + rowb, off.trlo[dt], off.trhi[dt]);
+                    const frag a = tr_frag<T>(ksl + rowb, o.tr(dt, 0), o.tr(dt, 1));
                     acc[dt] = Ty<T>::mma(a, ps ? d1 : d0, acc[dt]);
                 }
             }
@@ -312,19 +325,19 @@ __device__ __attribute__((always_inline)) inline void fa_bwd_dkdv_body(const Bwd
 
     Offs<D> off;
     off.init(lane);
-    int goff[PPW];
-#pragma unroll
-    for (int x = 0; x < PPW; ++x) goff[x] = dma_goff<D>(wave * PPW + x, lane);
+    const int goff0 = dma_goff<D>(wave * PPW, lane);
     const unsigned lds0 = (unsigned)(unsigned long long)(lds_char*)smem;
     float* stats = reinterpret_cast<float*>(smem + 4 * TILE);
     auto dma_tile = [&](int t) {                  // Q_t, dO_t into stage t & 1
         const i32x4 qr = buffer_rsrc_at(qh, L * P, t * TILE);
         const i32x4 gr = buffer_rsrc_at(gh, L * P, t * TILE);
+        int g0 = goff0;
+        asm volatile("" : "+v"(g0));              // derive the piece offsets here, not across the loop
 #pragma unroll
         for (int x = 0; x < PPW; ++x) {
             const unsigned dst = lds0 + (t & 1) * TILE + 1024 * (wave * PPW + x);
-            dma16(qr, goff[x], __builtin_amdgcn_readfirstlane(dst));
-            dma16(gr, goff[x], __builtin_amdgcn_readfirstlane(dst + 2 * TILE));
+            dma16(qr, g0 ^ (x * 0x440), __builtin_amdgcn_readfirstlane(dst));
+            dma16(gr, g0 ^ (x * 0x440), __builtin_amdgcn_readfirstlane(dst + 2 * TILE));
         }
     };
     // row statistics of tile t (wave 0): lse in base-2 units (+inf past L, so
@@ -350,45 +363,48 @@ __device__ __attribute__((always_inline)) inline void fa_bwd_dkdv_body(const Bwd
         const lds_char* qsl = (const lds_char*)smem + (t & 1) * TILE;
         const lds_char* gsl = (const lds_char*)smem + 2 * TILE + (t & 1) * TILE;
         const float* sl = stats + (t & 1) * 128 + 32 * qt;
+        const Offs<D> o = off.fresh();
         f32x16 st, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] = dp[r] = 0.f;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const frag a = __builtin_bit_cast(frag, ld16(qs + qt * 32 * P + off.row[s]));
-            const frag b = __builtin_bit_cast(frag, ld16(gs + qt * 32 * P + off.row[s]));
+            const frag a = __builtin_bit_cast(frag, ld16(qs + qt * 32 * P + o.row(s)));
+            const frag b = __builtin_bit_cast(frag, ld16(gs + qt * 32 * P + o.row(s)));
             st = Ty<T>::mma(a, kf[s], st);
             dp = Ty<T>::mma(b, vf[s], dp);
         }
-        // register r holds query t*64 + 32qt + 8(r/4) + 4hf + r%4 of key `key`
+        // register r holds query t*64 + 32qt + 8(r/4) + 4hf + r%4 of key `key`.
+        // P and dS are formed and consumed in two halves (registers 8ps..8ps+7,
+        // queries 16ps..16ps+15), each feeding its dV and dK products at once.
         const int first = t * 64 + 32 * qt + 4 * hf;
-        float pr[16], ds[16];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float4 l4 = *reinterpret_cast<const float4*>(sl + 8 * g + 4 * hf);
-            const float4 d4 = *reinterpret_cast<const float4*>(sl + 64 + 8 * g + 4 * hf);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * g + e;
-                float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], p.c, -lv[e]));
-                if (MASK && key > first + 8 * g + e) x = 0.f;
-                pr[r] = x;
-                ds[r] = x * (dp[r] - dv[e]);
-            }
-        }
-        const frag p0 = Ty<T>::cvt(pr), p1 = Ty<T>::cvt(pr + 8);
-        const frag s0 = Ty<T>::cvt(ds), s1 = Ty<T>::cvt(ds + 8);
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {
+            float pr[8], ds[8];
+#pragma unroll
+            for (int gg = 0; gg < 2; ++gg) {
+                const int g = 2 * ps + gg;
+                const float4 l4 = *reinterpret_cast<const float4*>(sl + 8 * g + 4 * hf);
+                const float4 d4 = *reinterpret_cast<const float4*>(sl + 64 + 8 * g + 4 * hf);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], p.c, -lv[e]));
+                    if (MASK && key > first + 8 * g + e) x = 0.f;
+                    pr[4 * gg + e] = x;
+                    ds[4 * gg + e] = x * (dp[r] - dv[e]);
+                }
+            }
+            const frag pf = Ty<T>::cvt(pr), sf = Ty<T>::cvt(ds);
             const int rowb = (qt * 32 + 16 * ps) * P;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                const frag ga = tr_frag<T>(gsl + rowb, off.trlo[dt], off.trhi[dt]);
-                dva[dt] = Ty<T>::mma(ga, ps ? p1 : p0, dva[dt]);
-                const frag qa = tr_frag<T>(qsl + rowb, off.trlo[dt], off.trhi[dt]);
-                dka[dt] = Ty<T>::mma(qa, ps ? s1 : s0, dka[dt]);
+                const frag ga = tr_frag<T>(gsl + rowb, o.tr(dt, 0), o.tr(dt, 1));
+                dva[dt] = Ty<T>::mma(ga, pf, dva[dt]);
+                const frag qa = tr_frag<T>(qsl + rowb, o.tr(dt, 0), o.tr(dt, 1));
+                dka[dt] = Ty<T>::mma(qa, sf, dka[dt]);
             }
         }
     };
@@ -448,16 +464,11 @@ __device__ __attribute__((always_inline)) inline void fa_bwd_dkdv_body(const Bwd
     }
 }
 
-// Two waves per SIMD where the registers allow it (non-causal); the causal
-// variant's masked diagonal tiles need more registers than that leaves.
+// Two waves per SIMD (256 registers a lane): with only the offset bases kept
+// across the tile loop, both variants fit without spilling inside it.
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
-    fa_bwd_dkdv_body<T, D, CAUSAL>(p);
-}
-template <class T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fa_bwd_dkdv1_kernel(BwdParams p) {
     fa_bwd_dkdv_body<T, D, CAUSAL>(p);
 }
 
@@ -475,10 +486,7 @@ int launch_bwd(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
     rc = fa_detail::launch_status();
     if (rc != FA_OK) return rc;
-    if constexpr (CAUSAL)
-        hipLaunchKernelGGL((fa_bwd_dkdv1_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
     return fa_detail::launch_status();
 }
 
