@@ -13,6 +13,10 @@ Contents
   * ``attn_range`` / ``merge`` -- one K/V block's attention for a few query
                  rows (rectangular, no mask) and the merge of such partial
                  results: the Flash-Decoding task and its combine step.
+  * ``e4m3_value`` / ``e4m3_code`` / ``quantize_fp8`` / ``fwd_fp8`` -- the
+                 E4M3 format, FP8 block quantisation of Q and K, and attention
+                 on the quantised Q and K (exact dequantisation, then ``fwd``'s
+                 definition).
   * ``tiled`` -- float64 NumPy models of the tiled online-softmax algorithm
                  itself, used only to pin that the tiled method is exact.
 
@@ -61,6 +65,14 @@ def _load():
         lib.fa_oracle_merge.restype = i
         lib.fa_oracle_bwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, d, i, vp, vp, vp, i]
         lib.fa_oracle_bwd.restype = i
+        lib.fa_oracle_e4m3_value.argtypes = [i]
+        lib.fa_oracle_e4m3_value.restype = d
+        lib.fa_oracle_e4m3_code.argtypes = [ctypes.c_float]
+        lib.fa_oracle_e4m3_code.restype = i
+        lib.fa_oracle_quantize_fp8.argtypes = [vp, i, i, i, i, i, i, vp, vp]
+        lib.fa_oracle_quantize_fp8.restype = i
+        lib.fa_oracle_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, i, vp, i, vp, vp, i]
+        lib.fa_oracle_fwd_fp8.restype = i
         lib.fa_oracle_max_threads.argtypes = []
         lib.fa_oracle_max_threads.restype = i
         _lib = lib
@@ -180,3 +192,58 @@ def bwd(q, k, v, dout, dtype: int, scale: float, causal: int, nthreads: int = 0)
     if rc != 0:
         raise ValueError(f"fa_oracle_bwd rejected its arguments (rc={rc})")
     return dq, dk, dv
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an E4M3 code (NaN for the NaN codes)."""
+    return _load().fa_oracle_e4m3_value(int(code))
+
+
+def e4m3_code(x: float) -> int:
+    """E4M3 code of a float32 value |x| <= 448, round to nearest even (-1 if out of range)."""
+    return _load().fa_oracle_e4m3_code(float(np.float32(x)))
+
+
+def quantize_fp8(x, dtype: int, block: int):
+    """Block quantisation of x (B, H, L, d) in storage type `dtype` to E4M3.
+
+    Returns codes uint8 (B, H, L, d) and float32 scales (B*H, ceil(L/block))."""
+    x = _storage_check(x, dtype)
+    B, H, L, d = x.shape
+    nblk = (L + block - 1) // block
+    x8 = np.empty((B, H, L, d), dtype=np.uint8)
+    sc = np.empty((B * H, nblk), dtype=np.float32)
+    rc = _load().fa_oracle_quantize_fp8(x.ctypes.data, dtype, B, H, L, d, int(block), x8.ctypes.data, sc.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"fa_oracle_quantize_fp8 rejected its arguments (rc={rc})")
+    return x8, sc
+
+
+def fwd_fp8(q8, k8, q_scale, k_scale, v, dtype: int, scale: float, causal: int, block_q: int, block_k: int,
+            rows=None, nthreads: int = 0):
+    """O (B,H,nrows,d) and lse (B,H,nrows), float64, of attention on the
+    dequantised q8 * q_scale and k8 * k_scale, with v in storage type `dtype`."""
+    q8 = np.ascontiguousarray(q8, dtype=np.uint8)
+    k8 = np.ascontiguousarray(k8, dtype=np.uint8)
+    v = _storage_check(v, dtype)
+    B, H, L, d = q8.shape
+    if k8.shape != q8.shape or v.shape != q8.shape:
+        raise ValueError("q8, k8, v must share one (B, H, L, d) shape")
+    sq = np.ascontiguousarray(q_scale, dtype=np.float32)
+    sk = np.ascontiguousarray(k_scale, dtype=np.float32)
+    if sq.size != B * H * ((L + block_q - 1) // block_q) or sk.size != B * H * ((L + block_k - 1) // block_k):
+        raise ValueError("scale arrays must hold B*H*ceil(L/block) values")
+    if rows is None:
+        nrows, rows_arr, rows_ptr = L, None, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int32)
+        nrows = int(rows_arr.size)
+        rows_ptr = rows_arr.ctypes.data
+    o = np.empty((B, H, nrows, d), dtype=np.float64)
+    lse = np.empty((B, H, nrows), dtype=np.float64)
+    rc = _load().fa_oracle_fwd_fp8(q8.ctypes.data, k8.ctypes.data, sq.ctypes.data, sk.ctypes.data, v.ctypes.data,
+                                   dtype, B, H, L, d, float(scale), int(causal), int(block_q), int(block_k),
+                                   rows_ptr, nrows, o.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"fa_oracle_fwd_fp8 rejected its arguments (rc={rc})")
+    return o, lse

@@ -54,82 +54,96 @@ int fa_oracle_max_threads(void) {
 #endif
 }
 
+/* One head: rows `rows` (NULL: all L) of qd against kd, vd, all (L x d)
+ * float64.  oh : (nrows x d), lseh : (nrows). */
+static void attend_head(const double* qd, const double* kd, const double* vd, int L, int d, double scale,
+                        int causal, const int* rows, int nrows, double* oh, double* lseh, int nthreads) {
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* s = (double*)malloc((size_t)L * sizeof(double));
+        double* p = (double*)malloc((size_t)L * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < nrows; ++r) {
+            const int i = rows ? rows[r] : r;
+            const double* qi = qd + (size_t)i * d;
+
+            /* S row: scale * q_i . k_j ; causal keys after the query are -inf */
+            for (int j = 0; j < L; ++j) {
+                if (causal && j > i) {
+                    s[j] = -INFINITY;
+                    continue;
+                }
+                double dot = 0.0;
+                const double* kj = kd + (size_t)j * d;
+                for (int c = 0; c < d; ++c) dot += qi[c] * kj[c];
+                s[j] = scale * dot;
+            }
+            /* row maximum */
+            double m = -INFINITY;
+            for (int j = 0; j < L; ++j)
+                if (s[j] > m) m = s[j];
+            /* exponentials relative to the maximum, and their sum */
+            double l = 0.0;
+            for (int j = 0; j < L; ++j) {
+                p[j] = exp(s[j] - m);
+                l += p[j];
+            }
+            /* O row = (P row . V) / l */
+            double* oi = oh + (size_t)r * d;
+            for (int c = 0; c < d; ++c) oi[c] = 0.0;
+            for (int j = 0; j < L; ++j) {
+                const double* vj = vd + (size_t)j * d;
+                for (int c = 0; c < d; ++c) oi[c] += p[j] * vj[c];
+            }
+            for (int c = 0; c < d; ++c) oi[c] /= l;
+            lseh[r] = m + log(l);
+        }
+        free(s);
+        free(p);
+    }
+}
+
+static int check_rows(int L, const int* rows, int nrows) {
+    if (nrows <= 0 || (!rows && nrows != L)) return -1;
+    if (rows) {
+        for (int r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= L) return -1;
+    }
+    return 0;
+}
+
 int fa_oracle_fwd(const void* q, const void* k, const void* v, int dtype,
                   int B, int H, int L, int d, double scale, int causal,
                   const int* rows, int nrows, double* o, double* lse, int nthreads) {
     if (!q || !k || !v || !o || !lse) return -1;
     if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16 && dtype != ORACLE_F64)
         return -1;
-    if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || nrows <= 0) return -1;
+    if (B <= 0 || H <= 0 || L <= 0 || d <= 0) return -1;
     if (causal != 0 && causal != 1) return -1;
-    if (!rows && nrows != L) return -1;
-    if (rows) {
-        for (int r = 0; r < nrows; ++r)
-            if (rows[r] < 0 || rows[r] >= L) return -1;
-    }
+    if (check_rows(L, rows, nrows)) return -1;
     if (nthreads <= 0) nthreads = fa_oracle_max_threads();
 
     const size_t head = (size_t)L * (size_t)d;
+    double* qd = (double*)malloc(head * sizeof(double));
     double* kd = (double*)malloc(head * sizeof(double));
     double* vd = (double*)malloc(head * sizeof(double));
-    if (!kd || !vd) {
+    if (!qd || !kd || !vd) {
+        free(qd);
         free(kd);
         free(vd);
         return -1;
     }
-
     for (int bh = 0; bh < B * H; ++bh) {
         const size_t base = (size_t)bh * head;
         for (size_t e = 0; e < head; ++e) {
+            qd[e] = widen(q, dtype, base + e);
             kd[e] = widen(k, dtype, base + e);
             vd[e] = widen(v, dtype, base + e);
         }
-#pragma omp parallel num_threads(nthreads)
-        {
-            double* qi = (double*)malloc((size_t)d * sizeof(double));
-            double* s = (double*)malloc((size_t)L * sizeof(double));
-            double* p = (double*)malloc((size_t)L * sizeof(double));
-#pragma omp for schedule(dynamic, 1)
-            for (int r = 0; r < nrows; ++r) {
-                const int i = rows ? rows[r] : r;
-                for (int c = 0; c < d; ++c) qi[c] = widen(q, dtype, base + (size_t)i * d + c);
-
-                /* S row: scale * q_i . k_j ; causal keys after the query are -inf */
-                for (int j = 0; j < L; ++j) {
-                    if (causal && j > i) {
-                        s[j] = -INFINITY;
-                        continue;
-                    }
-                    double dot = 0.0;
-                    const double* kj = kd + (size_t)j * d;
-                    for (int c = 0; c < d; ++c) dot += qi[c] * kj[c];
-                    s[j] = scale * dot;
-                }
-                /* row maximum */
-                double m = -INFINITY;
-                for (int j = 0; j < L; ++j)
-                    if (s[j] > m) m = s[j];
-                /* exponentials relative to the maximum, and their sum */
-                double l = 0.0;
-                for (int j = 0; j < L; ++j) {
-                    p[j] = exp(s[j] - m);
-                    l += p[j];
-                }
-                /* O row = (P row . V) / l */
-                double* oi = o + ((size_t)bh * nrows + r) * d;
-                for (int c = 0; c < d; ++c) oi[c] = 0.0;
-                for (int j = 0; j < L; ++j) {
-                    const double* vj = vd + (size_t)j * d;
-                    for (int c = 0; c < d; ++c) oi[c] += p[j] * vj[c];
-                }
-                for (int c = 0; c < d; ++c) oi[c] /= l;
-                lse[(size_t)bh * nrows + r] = m + log(l);
-            }
-            free(qi);
-            free(s);
-            free(p);
-        }
+        attend_head(qd, kd, vd, L, d, scale, causal, rows, nrows, o + (size_t)bh * nrows * d,
+                    lse + (size_t)bh * nrows, nthreads);
     }
+    free(qd);
     free(kd);
     free(vd);
     return 0;
@@ -346,5 +360,114 @@ int fa_oracle_bwd(const void* q, const void* k, const void* v, const void* dout,
         }
     }
     free(qd); free(kd); free(vd); free(gd); free(P); free(dS);
+    return 0;
+}
+
+/* ---- FP8 (E4M3) block quantisation and attention on the quantised Q, K ---- */
+
+double fa_oracle_e4m3_value(int code) {
+    if (code < 0 || code > 255) return NAN;
+    const int sign = code >> 7, ex = (code >> 3) & 15, man = code & 7;
+    if (ex == 15 && man == 7) return NAN;
+    /* exponent field 0: subnormal man/8 * 2^-6; else (1 + man/8) * 2^(ex-7) */
+    const double mag = ex == 0 ? ldexp((double)man, -9) : ldexp((double)(8 + man), ex - 10);
+    return sign ? -mag : mag;
+}
+
+int fa_oracle_e4m3_code(float x) {
+    if (!(fabsf(x) <= 448.0f)) return -1;       /* NaN or out of range */
+    const int sign = signbit(x) ? 1 : 0;
+    const double a = fabs((double)x);
+    if (a == 0.0) return sign << 7;
+    int e2;
+    (void)frexp(a, &e2);                        /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;                             /* a = 1.x * 2^e */
+    if (e < -6) e = -6;                         /* subnormals share the quantum of the smallest binade */
+    const double quantum = ldexp(1.0, e - 3);   /* 3 fraction bits */
+    double m = nearbyint(a / quantum);          /* exact quotient; ties to even (default rounding mode) */
+    /* m counts quanta: [8, 16] in a normal binade, [0, 8] in the subnormal one */
+    if (m >= 16.0) {                            /* rounded up into the next binade */
+        m = 8.0;
+        e += 1;
+    }
+    int code;
+    if (m < 8.0) {
+        code = (int)m;                          /* subnormal: exponent field 0 */
+    } else {
+        code = ((e + 7) << 3) | ((int)m - 8);
+    }
+    return (sign << 7) | code;
+}
+
+int fa_oracle_quantize_fp8(const void* x, int dtype, int B, int H, int L, int d, int block,
+                           unsigned char* x8, float* scales) {
+    if (!x || !x8 || !scales) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || block <= 0) return -1;
+    const int nblk = (L + block - 1) / block;
+    for (int bh = 0; bh < B * H; ++bh) {
+        for (int b = 0; b < nblk; ++b) {
+            const int r0 = b * block, r1 = r0 + block < L ? r0 + block : L;
+            const size_t e0 = ((size_t)bh * L + r0) * d, e1 = ((size_t)bh * L + r1) * d;
+            /* amax over the block (the stored values are exact in float32) */
+            float amax = 0.0f;
+            for (size_t e = e0; e < e1; ++e) {
+                const float a = fabsf((float)widen(x, dtype, e));
+                if (a > amax) amax = a;
+            }
+            /* s = amax / 448 in float32; an all-zero block takes s = 1 */
+            const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+            scales[(size_t)bh * nblk + b] = s;
+            for (size_t e = e0; e < e1; ++e) {
+                float y = (float)widen(x, dtype, e) / s;     /* float32 quotient */
+                if (y > 448.0f) y = 448.0f;
+                if (y < -448.0f) y = -448.0f;
+                x8[e] = (unsigned char)fa_oracle_e4m3_code(y);
+            }
+        }
+    }
+    return 0;
+}
+
+int fa_oracle_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const float* q_scale, const float* k_scale,
+                      const void* v, int dtype, int B, int H, int L, int d, double scale, int causal,
+                      int block_q, int block_k, const int* rows, int nrows, double* o, double* lse, int nthreads) {
+    if (!q8 || !k8 || !q_scale || !k_scale || !v || !o || !lse) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
+    if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || block_q <= 0 || block_k <= 0) return -1;
+    if (causal != 0 && causal != 1) return -1;
+    if (check_rows(L, rows, nrows)) return -1;
+    if (nthreads <= 0) nthreads = fa_oracle_max_threads();
+    const int nbq = (L + block_q - 1) / block_q, nbk = (L + block_k - 1) / block_k;
+    const size_t head = (size_t)L * (size_t)d;
+    double* qd = (double*)malloc(head * sizeof(double));
+    double* kd = (double*)malloc(head * sizeof(double));
+    double* vd = (double*)malloc(head * sizeof(double));
+    if (!qd || !kd || !vd) {
+        free(qd);
+        free(kd);
+        free(vd);
+        return -1;
+    }
+    for (int bh = 0; bh < B * H; ++bh) {
+        const size_t base = (size_t)bh * head;
+        /* dequantise: code value times its block's scale (exact in float64:
+         * 4 significant bits times 24) */
+        for (int i = 0; i < L; ++i) {
+            const double sq = q_scale[(size_t)bh * nbq + i / block_q];
+            const double sk = k_scale[(size_t)bh * nbk + i / block_k];
+            for (int c = 0; c < d; ++c) {
+                const size_t e = (size_t)i * d + c;
+                qd[e] = fa_oracle_e4m3_value(q8[base + e]) * sq;
+                kd[e] = fa_oracle_e4m3_value(k8[base + e]) * sk;
+                vd[e] = widen(v, dtype, base + e);
+            }
+        }
+        attend_head(qd, kd, vd, L, d, scale, causal, rows, nrows, o + (size_t)bh * nrows * d,
+                    lse + (size_t)bh * nrows, nthreads);
+    }
+    free(qd);
+    free(kd);
+    free(vd);
     return 0;
 }

@@ -106,6 +106,52 @@ int fa_oracle_bwd(const void* q, const void* k, const void* v, const void* dout,
                   int B, int H, int L, int d, double scale, int causal,
                   double* dq, double* dk, double* dv, int nthreads);
 
+/*
+ * FP8 block quantisation ("FlashAttention 深度解析", third article
+ * (FlashAttention-3), section 2.3): Q and K are cut into blocks, each block is scaled
+ * into the FP8 range on its own, s = max|block| / FP8_MAX and
+ * X_FP8 = Quantize(X_block / s), and the scores are dequantised after the
+ * product: S = (Q_FP8 K_FP8^T) * s_q * s_k * scale.
+ *
+ * The format is E4M3 as the OCP 8-bit floating point specification defines
+ * it: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits, exponent field 0
+ * for zero and subnormals (fraction/8 * 2^-6), no infinities, S.1111.111 the
+ * only NaN, so the largest finite value (FP8_MAX) is 1.75 * 2^8 = 448.
+ */
+
+/* Value of an E4M3 code (0..255); NaN for the NaN codes and out-of-range codes. */
+double fa_oracle_e4m3_value(int code);
+
+/* E4M3 code of a finite float with |x| <= 448, rounded to nearest, ties to
+ * even (the even code is the one whose last fraction bit is 0); -0.0 gives
+ * 0x80.  Returns -1 for NaN or |x| > 448. */
+int fa_oracle_e4m3_code(float x);
+
+/*
+ * Quantise x (B, H, L, d) in blocks of `block` consecutive rows of one
+ * (b, h) (the last block of a head may be short), all d columns of a row in
+ * its block.  Per block, in float32: amax = max |x|; s = amax / 448 (s = 1
+ * for an all-zero block); each element's code is e4m3_code(clamp(x / s,
+ * -448, 448)) (the clamp only absorbs the rounding of s).
+ * x8 : (B, H, L, d) codes; scales : float32 (B*H, ceil(L / block)).
+ * dtype: float32, float16 or bfloat16 storage.  Returns 0, or -1 on a bad
+ * argument.
+ */
+int fa_oracle_quantize_fp8(const void* x, int dtype, int B, int H, int L, int d, int block,
+                           unsigned char* x8, float* scales);
+
+/*
+ * Attention on block-quantised Q and K: the definition of fa_oracle_fwd with
+ * q_ic = e4m3_value(q8_ic) * q_scale[bh][i / block_q] and
+ * k_jc = e4m3_value(k8_jc) * k_scale[bh][j / block_k] (both exact in
+ * float64), v widened from its storage type.
+ * q8, k8 : (B, H, L, d) codes; q_scale : (B*H, ceil(L/block_q));
+ * k_scale : (B*H, ceil(L/block_k)); rows, o, lse as for fa_oracle_fwd.
+ */
+int fa_oracle_fwd_fp8(const unsigned char* q8, const unsigned char* k8, const float* q_scale, const float* k_scale,
+                      const void* v, int dtype, int B, int H, int L, int d, double scale, int causal,
+                      int block_q, int block_k, const int* rows, int nrows, double* o, double* lse, int nthreads);
+
 /* Threads an fa_oracle_fwd call with nthreads <= 0 would use. */
 int fa_oracle_max_threads(void);
 
