@@ -299,6 +299,137 @@ def bench_bwd(args, torch, fa, cfg):
     print(json.dumps(out), flush=True)
 
 
+# Peak of the FP8 forward's MFMA work: half its FLOPs (S = Q K^T) run on E4M3
+# operands (5.0 PFLOP/s dense on MI355X), half (P V) on 16-bit ones (2.5166),
+# so at both peaks a launch takes F/2/5000 + F/2/2516.6 and the combined peak is
+# the harmonic mean 2 / (1/5000 + 1/2516.6).
+FP8_MIXED_PEAK = 2.0 / (1.0 / 5000.0 + 1.0 / 2516.6)
+
+
+def cpu_baseline_fp8(cfg, q, k, v, target_s: float):
+    """The oracle (quantiser, then attention on the quantised Q, K) on a bounded
+    sample of query rows of every head."""
+    import oracle
+    nth = oracle.max_threads()
+    per_row = 4.0 * cfg.L * cfg.d * (0.5 if cfg.causal else 1.0)
+    t = time.perf_counter()
+    q8, sq = oracle.quantize_fp8(q, cfg.dtype, cfg.block_q)
+    k8, sk = oracle.quantize_fp8(k, cfg.dtype, cfg.block_k)
+    tq = time.perf_counter() - t
+    rows0 = gen.sample_rows(cfg.L, min(64, cfg.L), cfg.seed)
+    t = time.perf_counter()
+    oracle.fwd_fp8(q8, k8, sq, sk, v, cfg.dtype, cfg.scale, cfg.causal, cfg.block_q, cfg.block_k, rows0)
+    t0 = max(time.perf_counter() - t, 1e-3)
+    nrows = int(min(cfg.L, max(16, rows0.size * target_s / t0)))
+    rows = gen.sample_rows(cfg.L, nrows, cfg.seed)
+    t = time.perf_counter()
+    oracle.fwd_fp8(q8, k8, sq, sk, v, cfg.dtype, cfg.scale, cfg.causal, cfg.block_q, cfg.block_k, rows)
+    dt = time.perf_counter() - t
+    flops = per_row * rows.size * cfg.B * cfg.H
+    return {
+        "value": flops / (dt + tq * rows.size / cfg.L) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": nth,
+        "kind": "oracle",
+        "sample": (f"quantisation of all of Q and K ({tq:.1f} s, charged pro rata), then {rows.size} query rows "
+                   f"per head x {cfg.B * cfg.H} heads (all L={cfg.L} keys each), fp64 C oracle, OpenMP; "
+                   f"{dt:.1f} s"),
+        "seconds": dt,
+        "cpu_model": _cpu_model(),
+        "nproc": os.cpu_count(),
+    }
+
+
+def bench_fp8(args, torch, fa, cfg):
+    """The FP8 forward: one step quantises Q and K (fa_quantize_fp8, two
+    launches) and runs fa_fwd_fp8 on the codes and the 16-bit V."""
+    log(f"[bench] fp8: {cfg.name}; generating inputs")
+    q, k, v = gen.make_fp8_inputs(cfg)
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    qd, kd, vd = (dev(x) for x in (q, k, v))
+    B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
+    q8 = torch.empty(qd.shape, dtype=torch.uint8, device="cuda")
+    k8 = torch.empty_like(q8)
+    sq = torch.empty((B * H, (L + cfg.block_q - 1) // cfg.block_q), dtype=torch.float32, device="cuda")
+    sk = torch.empty((B * H, (L + cfg.block_k - 1) // cfg.block_k), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(vd)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    quant_q = (qd.data_ptr(), cfg.dtype, B, H, L, d, cfg.block_q, q8.data_ptr(), sq.data_ptr(), sh)
+    quant_k = (kd.data_ptr(), cfg.dtype, B, H, L, d, cfg.block_k, k8.data_ptr(), sk.data_ptr(), sh)
+    attn = (q8.data_ptr(), k8.data_ptr(), sq.data_ptr(), sk.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            B, H, L, d, float(cfg.scale), cfg.causal, cfg.dtype, cfg.block_q, cfg.block_k, sh)
+
+    def step():
+        rc = fa.fa_quantize_fp8(*quant_q) or fa.fa_quantize_fp8(*quant_k) or fa.fa_fwd_fp8(*attn)
+        if rc != 0:
+            raise SystemExit(f"FP8 step failed: {rc} {fa.fa_strerror(rc)}")
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    log(f"[bench] timing {args.steps} steps")
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    # the attention kernel alone, same inputs, same stream
+    ev[2].record(stream)
+    for _ in range(args.steps):
+        fa.fa_fwd_fp8(*attn)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    ms_attn = ev[2].elapsed_time(ev[3]) / args.steps
+    tflops = cfg.flops / (ms * 1e-3) / 1e12
+    tflops_attn = cfg.flops / (ms_attn * 1e-3) / 1e12
+    peak = FP8_MIXED_PEAK
+    log(f"[bench] step {ms:.4f} ms ({tflops:.1f} TFLOP/s); attention kernel {ms_attn:.4f} ms "
+        f"({tflops_attn:.1f} TFLOP/s, {100 * tflops_attn / peak:.1f}% of the {peak:.0f} mixed FP8/bf16 peak)")
+    out = {
+        "metric": "attention fwd TFLOP/s (4*B*H*L^2*d) with Q, K block-quantised to FP8 E4M3 (quantisation "
+                  "included) and % of the mixed FP8/bf16 MFMA peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 (Q, K) + bf16 (V, P)",
+        "data": "synthetic (seeded SplitMix64 + Box-Muller normals)",
+        "config": {"workload": cfg.name, "B": B, "H": H, "L": L, "d": d, "causal": bool(cfg.causal),
+                   "scale": cfg.scale, "sigma_qkv": [cfg.sigma_q, cfg.sigma_k, cfg.sigma_v],
+                   "block_q": cfg.block_q, "block_k": cfg.block_k,
+                   "attention_kernel_ms": ms_attn, "quantise_ms": ms - ms_attn},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": tflops_attn,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": tflops_attn / peak,
+            "traffic": None,
+            "kernel": "fa_fwd_h_kernel (FP8 scores)",
+            "per_launch_flops": cfg.flops,
+            "avg_launch_ms": ms_attn,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle quantiser + attention on a sample of rows)")
+        out["cpu_baseline"] = cpu_baseline_fp8(cfg, q, k, v, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,7 +437,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="3",
                     help="workload index 0..4 (default 3); 'decode' (split-K/V decoding shape); "
-                         "'bwd' / 'bwd-causal' (backward pass shapes)")
+                         "'bwd' / 'bwd-causal' (backward pass shapes); 'fp8' / 'fp8-causal' (FP8 forward)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -339,6 +470,8 @@ def main():
         return bench_decode(args, torch, fa)
     if args.workload in ("bwd", "bwd-causal"):
         return bench_bwd(args, torch, fa, gen.BWD[0 if args.workload == "bwd" else 1])
+    if args.workload in ("fp8", "fp8-causal"):
+        return bench_fp8(args, torch, fa, gen.FP8[0 if args.workload == "fp8" else 1])
     cfg = gen.config(int(args.workload))
     log(f"[bench] workload {cfg.index}: {cfg.name}; generating inputs")
     q, k, v = gen.make_qkv(cfg)

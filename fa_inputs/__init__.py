@@ -29,7 +29,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from .configs import BWD, CONFIGS, DECODE, BwdConfig, Config, DecodeConfig, config  # noqa: F401
+from .configs import BWD, CONFIGS, DECODE, FP8, BwdConfig, Config, DecodeConfig, Fp8Config, config  # noqa: F401
 
 F32, F16, BF16 = 0, 1, 2
 DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
@@ -189,3 +189,10 @@ def make_bwd_inputs(cfg):
     """Q, K, V and dO storage arrays (B, H, L, d) for a backward shape."""
     shape = (cfg.B, cfg.H, cfg.L, cfg.d)
     return tuple(fill(cfg.dtype, shape, cfg.seed, s) for s in range(4))
+
+
+def make_fp8_inputs(cfg):
+    """Q, K, V storage arrays (B, H, L, d) in cfg.dtype for an FP8 shape (before quantisation)."""
+    shape = (cfg.B, cfg.H, cfg.L, cfg.d)
+    return (fill(cfg.dtype, shape, cfg.seed, 0, cfg.sigma_q), fill(cfg.dtype, shape, cfg.seed, 1, cfg.sigma_k),
+            fill(cfg.dtype, shape, cfg.seed, 2, cfg.sigma_v))

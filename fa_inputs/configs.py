@@ -124,3 +124,41 @@ BWD = [
     BwdConfig("bwd bf16 B1 H32 L8192 d128", 1, 32, 8192, 128, 2, 0, 1.0 / math.sqrt(128.0), 20),
     BwdConfig("bwd bf16 causal B2 H32 L4096 d128", 2, 32, 4096, 128, 2, 1, 1.0 / math.sqrt(128.0), 21),
 ]
+
+
+@dataclass(frozen=True)
+class Fp8Config:
+    """An FP8 forward shape: Q and K block-quantised to E4M3 (blocks of
+    block_q / block_k rows of a head), V and O in `dtype`.  The inputs are
+    those of the 16-bit workload with the same seed and value scales."""
+    name: str
+    B: int
+    H: int
+    L: int
+    d: int
+    dtype: int
+    causal: int
+    scale: float
+    seed: int
+    sigma_q: float
+    sigma_k: float
+    sigma_v: float
+    block_q: int
+    block_k: int
+    check_rows: int
+
+    @property
+    def flops(self) -> int:
+        """Metric FLOPs as for the 16-bit forward: 4*B*H*L^2*d, halved when causal."""
+        f = 4 * self.B * self.H * self.L * self.L * self.d
+        return f // 2 if self.causal else f
+
+
+# FP8 shapes: the peaked B1 H32 L8192 d128 workload (seed 3) and the causal
+# B2 H32 L4096 d128 one (seed 2), quantised in blocks of 128 rows.
+FP8 = [
+    Fp8Config("fp8 e4m3 q/k, bf16 v, peaked B1 H32 L8192 d128", 1, 32, 8192, 128, 2, 0, 1.0 / math.sqrt(128.0),
+              3, 3.0, 3.0, 1.0, 128, 128, 256),
+    Fp8Config("fp8 e4m3 q/k, bf16 v, causal B2 H32 L4096 d128", 2, 32, 4096, 128, 2, 1, 1.0 / math.sqrt(128.0),
+              2, 1.0, 1.0, 1.0, 128, 128, 256),
+]

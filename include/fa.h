@@ -203,6 +203,64 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dq, void* dk, void* dv, int B, int H, int L, int d, float scale, int causal, int dtype,
            void* workspace, size_t workspace_size, hipStream_t stream);
 
+/*
+ * ---- FP8 block-quantised forward pass ----
+ *
+ * "FlashAttention 深度解析", third article (FlashAttention-3), section 2.3:
+ * Q and K are cut into blocks, each block is scaled into the E4M3 range on
+ * its own, s = max|block| / 448 and codes = Quantize(block / s), and the
+ * scores are dequantised after the product:
+ *     S_ij = scale * s_q(block of i) * s_k(block of j) * (q8_i . k8_j)
+ * where q8_i, k8_j are the E4M3 values of the codes.  The rest is fa_fwd's
+ * operation with this S (mask, softmax, O = P V, lse).  V and O stay 16-bit
+ * (the section gives the quantisation for Q and K only).
+ *
+ * E4M3 is the OCP 8-bit floating point format: 1 sign, 4 exponent (bias 7)
+ * and 3 fraction bits, no infinities, largest finite value 448.
+ */
+
+/*
+ * fa_quantize_fp8 -- enqueue block quantisation of x on `stream`.
+ *
+ * x      : device, read only, (B, H, L, d) in `dtype` (FA_F16 or FA_BF16),
+ *          layout as for fa_fwd; finite values.
+ * block  : rows per block (>= 1).  A block is `block` consecutive rows of
+ *          one (b, h), all d columns; the last block of a head may be short.
+ * x8     : device, (B, H, L, d) bytes, fully overwritten with E4M3 codes:
+ *          code = E4M3(clamp(x / s, -448, 448)), round to nearest even, with
+ *          the float32 quotient of x by its block's s.
+ * scales : device float32 (B*H, ceil(L/block)), fully overwritten:
+ *          s = amax / 448 in float32, amax = max |x| over the block; s = 1
+ *          for an all-zero block.
+ * Ownership, asynchrony and errors as for fa_fwd: x and x8 16-byte aligned,
+ * scales 4-byte aligned; d not 64/128 or dtype not 16-bit returns
+ * FA_ERR_UNSUPPORTED; block < 1 or B*H > 65535 returns FA_ERR_INVALID_ARG.
+ */
+int fa_quantize_fp8(const void* x, int dtype, int B, int H, int L, int d, int block, void* x8,
+                    float* scales, hipStream_t stream);
+
+/*
+ * fa_fwd_fp8 -- enqueue the FP8 forward pass on `stream`.
+ *
+ * q8, k8  : device, read only, (B, H, L, d) E4M3 codes (as fa_quantize_fp8
+ *           writes them).
+ * q_scale : device float32 (B*H, ceil(L/block_q)); k_scale : device float32
+ *           (B*H, ceil(L/block_k)); finite and > 0.
+ * v       : device, read only, (B, H, L, d) in `dtype`.
+ * o, lse  : outputs as for fa_fwd (o in `dtype`).
+ * block_q : query rows per q_scale block (>= 1); block_k : key rows per
+ *           k_scale block, a multiple of 32 (one scale per 32-key MFMA
+ *           block).
+ * B, H, L, d, scale, causal as for fa_fwd; dtype FA_F16 or FA_BF16
+ * (FA_F32 returns FA_ERR_UNSUPPORTED).
+ * Ownership, asynchrony and errors as for fa_fwd: q8, k8, v and o 16-byte
+ * aligned, the float arrays 4-byte aligned; a bad block size returns
+ * FA_ERR_INVALID_ARG.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const float* q_scale, const float* k_scale, const void* v,
+               void* o, float* lse, int B, int H, int L, int d, float scale, int causal, int dtype,
+               int block_q, int block_k, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

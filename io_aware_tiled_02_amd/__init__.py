@@ -53,6 +53,10 @@ def load():
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
         lib.fa_bwd.restype = i
+        lib.fa_quantize_fp8.argtypes = [vp, i, i, i, i, i, i, vp, vp, vp]
+        lib.fa_quantize_fp8.restype = i
+        lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, vp]
+        lib.fa_fwd_fp8.restype = i
         _lib = lib
     return _lib
 
@@ -91,6 +95,18 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, L, d, scale, causal, dtype, 
     """The C entry point as is (raw device addresses and stream handle)."""
     return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, L, d, scale, causal, dtype, workspace,
                          workspace_size, stream)
+
+
+def fa_quantize_fp8(x, dtype, B, H, L, d, block, x8, scales, stream) -> int:
+    """The C entry point as is (raw device addresses and stream handle)."""
+    return load().fa_quantize_fp8(x, dtype, B, H, L, d, block, x8, scales, stream)
+
+
+def fa_fwd_fp8(q8, k8, q_scale, k_scale, v, o, lse, B, H, L, d, scale, causal, dtype, block_q, block_k,
+               stream) -> int:
+    """The C entry point as is (raw device addresses and stream handle)."""
+    return load().fa_fwd_fp8(q8, k8, q_scale, k_scale, v, o, lse, B, H, L, d, scale, causal, dtype, block_q,
+                             block_k, stream)
 
 
 def fa_strerror(code: int) -> str:
@@ -200,3 +216,53 @@ def backward(q, k, v, o, lse, dout, scale: float, causal: bool = False, workspac
     if rc != FA_OK:
         raise FAError(rc, fa_strerror(rc))
     return dq, dk, dv
+
+
+def quantize_fp8(x, block: int, x8=None, scales=None, stream=None):
+    """E4M3 codes (uint8, x's shape) and float32 block scales (B*H, ceil(L/block))
+    of a 16-bit device tensor x (B, H, L, d)."""
+    import torch
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous (B, H, L, d) device tensor")
+    B, H, L, d = x.shape
+    if x8 is None:
+        x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B * H, (L + block - 1) // block), dtype=torch.float32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    rc = fa_quantize_fp8(x.data_ptr(), _dtype_code(x), B, H, L, d, int(block), x8.data_ptr(), scales.data_ptr(),
+                         stream.cuda_stream)
+    if rc != FA_OK:
+        raise FAError(rc, fa_strerror(rc))
+    return x8, scales
+
+
+def forward_fp8(q8, k8, q_scale, k_scale, v, scale: float, causal: bool, block_q: int, block_k: int, out=None,
+                lse=None, stream=None):
+    """O (v's dtype) and lse of attention on block-quantised q8, k8 (uint8
+    E4M3 codes (B, H, L, d)) with their scales, and 16-bit v (B, H, L, d)."""
+    import torch
+    if q8.shape != k8.shape or q8.shape != v.shape or q8.dim() != 4:
+        raise ValueError("q8, k8, v must share one (B, H, L, d) shape")
+    if q8.dtype != torch.uint8 or k8.dtype != torch.uint8:
+        raise TypeError("q8 and k8 hold E4M3 codes as uint8")
+    for t in (q8, k8, q_scale, k_scale, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous device tensors")
+    B, H, L, d = q8.shape
+    if q_scale.numel() != B * H * ((L + block_q - 1) // block_q) or \
+            k_scale.numel() != B * H * ((L + block_k - 1) // block_k):
+        raise ValueError("scale tensors must hold B*H*ceil(L/block) float32 values")
+    if out is None:
+        out = torch.empty_like(v)
+    if lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=v.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(v.device)
+    rc = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(), v.data_ptr(),
+                    out.data_ptr(), lse.data_ptr(), B, H, L, d, float(scale), int(bool(causal)), _dtype_code(v),
+                    int(block_q), int(block_k), stream.cuda_stream)
+    if rc != FA_OK:
+        raise FAError(rc, fa_strerror(rc))
+    return out, lse

@@ -6,7 +6,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", n) for n in ("fa_fwd.hip", "fa_splitkv.hip", "fa_bwd.hip")]
+SRCS = [os.path.join(HERE, "csrc", n) for n in ("fa_fwd.hip", "fa_splitkv.hip", "fa_bwd.hip", "fa_quant.hip")]
 LIB = os.path.join(HERE, "libfa_fwd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -87,6 +87,11 @@ struct Params {
     int remap;    // 1: BH % 8 == 0, keep a head's tiles on one XCD
     float c;      // scale * log2(e)
     float scale;
+    // FP8 scores only: per-block scales of Q and K, (BH, nbq) and (BH, nbk)
+    // float32, blocks of bq query rows and bk key rows of a head
+    const float* qsc;
+    const float* ksc;
+    int bq, bk, nbq, nbk;
 };
 
 template <class T, int D, bool CAUSAL, int NQB, int NW, int NKB>
@@ -452,18 +457,51 @@ void fa_fwd_f32_kernel(Params p) {
 #define FA_H_NKB64 4
 #endif
 
-// Tile shape of the 16-bit kernel: 8 waves x 32 query rows, 32*NKB-key tiles.
-template <int D>
+// Tile shape of the 16-bit-V kernel: 8 waves x 32 query rows, 32*NKB-key
+// tiles.  FP8: Q and K are one-byte E4M3 codes, V stays 16-bit.
+template <int D, bool FP8 = false>
 struct HCfg {
     static constexpr int NW = 8, QPW = 32, BR = NW * QPW, NKB = (D == 128 ? FA_H_NKB128 : FA_H_NKB64), BC = 32 * NKB;
-    static constexpr int P = D * 2;                 // LDS row pitch (bytes)
-    static constexpr int TILE = BC * P;             // one K or V tile (bytes)
-    static constexpr int LPW = TILE / 1024 / NW;    // 1 KB DMA instructions per wave per tile
+    static constexpr int P = D * 2;                 // V row pitch in LDS (bytes)
+    static constexpr int PK = FP8 ? D : D * 2;      // Q and K row pitch (bytes)
+    static constexpr int TILE = BC * P;             // one V tile (bytes)
+    static constexpr int TILEK = BC * PK;           // one K tile (bytes)
+    static constexpr int LPW = TILE / 1024 / NW;    // 1 KB DMA instructions per wave per V tile
+    static constexpr int LPWK = TILEK / 1024 / NW;  // ... per K tile
+    static_assert(LPWK >= 1 && LPWK * NW * 1024 == TILEK, "tile must split into 1 KB pieces per wave");
     static_assert(LPW >= 1 && LPW * NW * 1024 == TILE, "tile must split into 1 KB pieces per wave");
     // LDS: K stage 0, K stage 1, V stage 0, V stage 1
-    static constexpr int BYTES = 4 * TILE;
+    static constexpr int BYTES = 2 * TILEK + 2 * TILE;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
+
+// Row layout of an FP8 K tile (rows of D bytes, 16-byte chunks XOR-swizzled):
+// the 16 rows one 16-lane pass of ds_read_b128 reads start in 256/D distinct
+// bank positions, and the swizzle gives rows sharing a position distinct
+// chunks, so a pass touches all 64 banks once.
+template <int D>
+struct K8Layout {
+    static constexpr int CPR = D / 16, RPB = 256 / D;
+    __device__ static inline int fk(int r) { return (r / RPB) & (CPR - 1); }
+};
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(4))) const float kconst_f32;   // read through the scalar cache
+
+// S^T += K Q^T over 64 d-values with E4M3 codes: the K row chunks (a0, a1)
+// and Q row chunks (b0, b1) hold 32 consecutive d-values of the lane's
+// half.  gfx950's f8f6f4 MFMA with format 0 (E4M3) for both operands and
+// no block scaling.
+__device__ inline f32x16 mma_e4m3(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c) {
+    const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+    const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+template <class F>
+__device__ inline f32x16 mma_e4m3(F a0, F a1, F b0, F b1, f32x16 c) {
+    return mma_e4m3(__builtin_bit_cast(u32x4, a0), __builtin_bit_cast(u32x4, a1), __builtin_bit_cast(u32x4, b0),
+                    __builtin_bit_cast(u32x4, b1), c);
+}
 
 // Issue order of the MFMA slices of one phase: the NPV slices of P V (whose
 // operands come from transposing LDS reads, the slower kind) are spread
@@ -492,14 +530,18 @@ struct SliceOrder {
 // busy with the softmax.  M(T) only finishes the last PV.  K_j and V_{j-1}
 // are read in phases 2j and 2j+1; the DMA for K_{j+1} and V_j goes into the
 // other stages during phase 2j and is complete by the end of phase 2j+1.
-template <class T, int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_h_kernel(Params p) {
-    using Cf = HCfg<D>;
+    using Cf = HCfg<D, FP8>;
     constexpr int QPW = Cf::QPW, BR = Cf::BR, NKB = Cf::NKB, BC = Cf::BC;
     constexpr int P = Cf::P, TILE = Cf::TILE, LPW = Cf::LPW;
+    constexpr int PK = Cf::PK, TILEK = Cf::TILEK, LPWK = Cf::LPWK;
     using Lay = HLayout<D>;
     using frag = typename Ty<T>::frag;
+    // 16-byte chunks of one Q or K row a lane holds for the score MFMAs:
+    // 16-bit, one per 16-wide d step; FP8, two per 64-wide d step
+    constexpr int NQC = FP8 ? D / 32 : D / 16;
 
     __shared__ __attribute__((aligned(1024))) char smem[Cf::BYTES];
 
@@ -514,10 +556,10 @@ void fa_fwd_h_kernel(Params p) {
     const int l32 = lane & 31;
     const int hf = lane >> 5;
     const long long head = (long long)bh * L * D;
-    const char* qh = p.q + head * 2;
-    const char* kh = p.k + head * 2;
+    const char* qh = p.q + head * (PK / D);
+    const char* kh = p.k + head * (PK / D);
     const char* vh = p.v + head * 2;
-    const i32x4 krs = buffer_rsrc(kh, L * P);
+    const i32x4 krs = buffer_rsrc(kh, L * PK);
 
     const int q0 = qt * BR;
     const int qw = q0 + wave * QPW;                 // this wave's first query row
@@ -526,19 +568,30 @@ void fa_fwd_h_kernel(Params p) {
     // K/V tiles this wave computes (0 for a wave entirely past L)
     const int ntw = qw >= L ? 0 : (CAUSAL ? (min(qw + QPW, L) + BC - 1) / BC : ntiles);
 
-    // Q fragments (B operand of S^T = K Q^T)
-    frag qf[D / 16];
+    // Q fragments (B operand of S^T = K Q^T).  Chunk s of the lane: 16-bit,
+    // elements 16s + 8hf .. +7; FP8, bytes 64(s/2) + 32hf + 16(s%2) .. +15.
+    frag qf[NQC];
     {
         const int row = qw + l32;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
+        for (int s = 0; s < NQC; ++s) {
             u32x4 raw = u32x4{0, 0, 0, 0};
-            if (row < L) raw = ld16(qh + ((long long)row * D + 16 * s + 8 * hf) * 2);
+            if constexpr (FP8) {
+                if (row < L) raw = ld16(qh + (long long)row * PK + 64 * (s >> 1) + 32 * hf + 16 * (s & 1));
+            } else {
+                if (row < L) raw = ld16(qh + ((long long)row * D + 16 * s + 8 * hf) * 2);
+            }
             qf[s] = __builtin_bit_cast(frag, raw);
         }
         // take the Q loads' wait here, once, instead of inside the K/V loop
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(qf[s]));
+        for (int s = 0; s < NQC; ++s) asm volatile("" : "+v"(qf[s]));
+    }
+    // FP8: this lane's query-block scale times scale*log2(e)
+    float cq = p.c;
+    if constexpr (FP8) {
+        cq = p.c * p.qsc[(long long)bh * p.nbq + min(qw + l32, L - 1) / p.bq];
+        asm volatile("" : "+v"(cq));
     }
 
     // DMA mapping: byte o = 1024*n + 16*lane of a tile holds row o/P, slot
@@ -557,22 +610,32 @@ void fa_fwd_h_kernel(Params p) {
         const int r = o / P, slot = (o % P) >> 4;
         kd0 = r * P + ((slot ^ Lay::fk(r)) << 4);
         vd0 = r * P + ((slot ^ Lay::fv(r)) << 4);
+        if constexpr (FP8) {        // K rows of D bytes, same 4-rows-per-piece-step argument
+            const int ok = 1024 * (wq * LPWK) + 16 * lane;
+            const int rk = ok / PK, slotk = (ok % PK) >> 4;
+            kd0 = rk * PK + ((slotk ^ K8Layout<D>::fk(rk)) << 4);
+        }
     }
-    auto kdma_off = [&](int x, int hi) { return (kd0 ^ (x * 0x440)) + hi * 4096 * LPW; };
+    auto kdma_off = [&](int x, int hi) { return (kd0 ^ (x * 0x440)) + hi * 4096 * LPWK; };
     auto vdma_off = [&](int x, int hi) { return vd0 + 1024 * x + hi * 4096 * LPW; };
     const unsigned lds0 = (unsigned)(unsigned long long)(lds_char*)smem;
     auto issue_k2 = [&](int j) {
-        const unsigned dst = lds0 + (j & 1) * TILE + 1024 * wq * LPW;
+        const unsigned dst = lds0 + (j & 1) * TILEK + 1024 * wq * LPWK;
 #pragma unroll
-        for (int x = 0; x < LPW; ++x) {
-            dma16(krs, kdma_off(x, 0) + j * TILE, __builtin_amdgcn_readfirstlane(dst + 1024 * x));
-            dma16(krs, kdma_off(x, 1) + j * TILE, __builtin_amdgcn_readfirstlane(dst + 4096 * LPW + 1024 * x));
+        for (int x = 0; x < LPWK; ++x) {
+            dma16(krs, kdma_off(x, 0) + j * TILEK, __builtin_amdgcn_readfirstlane(dst + 1024 * x));
+            dma16(krs, kdma_off(x, 1) + j * TILEK, __builtin_amdgcn_readfirstlane(dst + 4096 * LPWK + 1024 * x));
         }
     };
     // per-lane LDS read offsets
-    int koff[D / 16];
+    // K chunk s of the lane (as for qf): 16-bit chunk 2s + hf of row l32;
+    // FP8 chunk 4(s/2) + 2hf + s%2
+    int koff[NQC];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) koff[s] = l32 * P + (((2 * s + hf) ^ Lay::fk(l32)) << 4);
+    for (int s = 0; s < NQC; ++s) {
+        if constexpr (FP8) koff[s] = l32 * PK + (((4 * (s >> 1) + 2 * hf + (s & 1)) ^ K8Layout<D>::fk(l32)) << 4);
+        else koff[s] = l32 * P + (((2 * s + hf) ^ Lay::fk(l32)) << 4);
+    }
     int voffv[D / 32];
     {
         const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
@@ -580,7 +643,7 @@ void fa_fwd_h_kernel(Params p) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
             const int c = 4 * dt + 2 * (g & 1) + (q >> 1);
-            voffv[dt] = 2 * TILE + rrel * P + ((c ^ Lay::fv(rrel)) << 4) + 8 * (q & 1);   // V stages start at 2*TILE
+            voffv[dt] = 2 * TILEK + rrel * P + ((c ^ Lay::fv(rrel)) << 4) + 8 * (q & 1);   // V stages start at 2*TILEK
         }
     }
 
@@ -599,17 +662,20 @@ void fa_fwd_h_kernel(Params p) {
     // waits for them at the end of its X(t) (phase 2t+1); the barrier there
     // publishes the stages, which are first read in phase 2t+2.
     const bool feeder = group == 0;
-    constexpr int NPIECE = 4 * LPW;               // DMA instructions per wave for K_{t+1}, V_t
+    constexpr int NPIECE = 2 * LPWK + 2 * LPW;    // DMA instructions per wave for K_{t+1}, V_t
     auto dma_piece = [&](int t, int n) {          // n-th instruction of K_{t+1}, V_t
-        const int x = (n >> 1) % LPW, hi = n & 1;
+        const int hi = n & 1;
         // the descriptors move to the tile, so the per-lane offsets are loop-invariant
-        if (n < 2 * LPW) {
+        if (n < 2 * LPWK) {
+            const int x = n >> 1;
             if (t + 1 < ntiles) {
-                const unsigned dst = lds0 + ((t + 1) & 1) * TILE + 1024 * (wq * LPW + x) + hi * 4096 * LPW;
-                dma16(buffer_rsrc_at(kh, L * P, (t + 1) * TILE), kdma_off(x, hi), __builtin_amdgcn_readfirstlane(dst));
+                const unsigned dst = lds0 + ((t + 1) & 1) * TILEK + 1024 * (wq * LPWK + x) + hi * 4096 * LPWK;
+                dma16(buffer_rsrc_at(kh, L * PK, (t + 1) * TILEK), kdma_off(x, hi),
+                      __builtin_amdgcn_readfirstlane(dst));
             }
         } else {
-            const unsigned dst = lds0 + 2 * TILE + (t & 1) * TILE + 1024 * (wq * LPW + x) + hi * 4096 * LPW;
+            const int x = (n - 2 * LPWK) >> 1;
+            const unsigned dst = lds0 + 2 * TILEK + (t & 1) * TILE + 1024 * (wq * LPW + x) + hi * 4096 * LPW;
             dma16(buffer_rsrc_at(vh, L * P, t * TILE), vdma_off(x, hi), __builtin_amdgcn_readfirstlane(dst));
         }
     };
@@ -643,7 +709,7 @@ void fa_fwd_h_kernel(Params p) {
         constexpr bool PV = decltype(pv_tag)::value;
         constexpr bool SC = decltype(s_tag)::value;
         constexpr int PAR = decltype(par_tag)::value;
-        constexpr int GPT = D / 64;                       // score slices per 32-key sub-tile
+        constexpr int GPT = FP8 ? 1 : D / 64;             // score slices per 32-key sub-tile
         constexpr int NPV = PV ? 2 * NKB : 0;
         constexpr int NSL = NPV + (SC ? NKB * GPT : 0);
         constexpr SliceOrder<NPV, NSL - NPV> ord{};
@@ -651,8 +717,8 @@ void fa_fwd_h_kernel(Params p) {
         // sharing the SIMD fills the gaps
         __builtin_amdgcn_s_setprio(3);
         const int kst = PAR >= 0 ? PAR : (j & 1);
-        const lds_char* vs = (const lds_char*)smem + (1 - kst) * TILE;    // voffv holds the 2*TILE
-        const char* ks = smem + kst * TILE;
+        const lds_char* vs = (const lds_char*)smem + (1 - kst) * TILE;    // voffv holds the 2*TILEK
+        const char* ks = smem + kst * TILEK;
         frag buf[2][4];
         auto load = [&](int pos) {
             const int i = ord.v[pos];
@@ -665,6 +731,11 @@ void fa_fwd_h_kernel(Params p) {
                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vs + rowb + 8 * P + voffv[dt]));
                     buf[pos & 1][dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
+            } else if constexpr (FP8) {
+                const int kt = i - NPV;
+#pragma unroll
+                for (int x = 0; x < NQC; ++x)
+                    buf[pos & 1][x] = __builtin_bit_cast(frag, ld16(ks + kt * 32 * PK + koff[x]));
             } else {
                 const int g = i - NPV, kt = g / GPT, s0 = 4 * (g % GPT);
 #pragma unroll
@@ -677,6 +748,13 @@ void fa_fwd_h_kernel(Params p) {
             if (i < NPV) {
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = Ty<T>::mma(buf[pos & 1][dt], pf[i >> 1][i & 1], oacc[dt]);
+            } else if constexpr (FP8) {
+                const int kt = i - NPV;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+#pragma unroll
+                for (int m = 0; m < D / 64; ++m)
+                    sacc[kt] = mma_e4m3(buf[pos & 1][2 * m], buf[pos & 1][2 * m + 1], qf[2 * m], qf[2 * m + 1], sacc[kt]);
             } else {
                 const int g = i - NPV, kt = g / GPT, s0 = 4 * (g % GPT);
                 if (s0 == 0) {
@@ -695,12 +773,24 @@ void fa_fwd_h_kernel(Params p) {
             if (more) load(i + 1);
             exec(i);
             mfeed(j, i, NSL);
-            if (more) {
+            if (more && !FP8) {
                 const int rd = ord.v[i + 1] < NPV ? 2 : 1;    // LDS reads per MFMA
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
                     if (rd == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then LDS reads
+                    else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            } else if (more) {
+                // FP8 score slices hold D/64 (longer) MFMAs and D/32 reads;
+                // PV slices D/32 MFMAs with two reads each
+                const int nm = ord.v[i] < NPV ? D / 32 : D / 64;
+                const int rd = (ord.v[i + 1] < NPV ? D / 16 : D / 32) / nm;
+#pragma unroll
+                for (int x = 0; x < nm; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (rd == 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                    else if (rd == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                     else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
             }
@@ -725,14 +815,36 @@ void fa_fwd_h_kernel(Params p) {
                 for (int r = 0; r < 16; ++r)
                     if (32 * kt + 8 * (r >> 2) + (r & 3) > lim) sacc[kt][r] = -INFINITY;
         }
-        float mx = sacc[0][0];
+        // score factor per 32-key sub-tile: scale*log2(e), times the query
+        // and key block scales for FP8 (one key block per sub-tile)
+        float ck[NKB];
 #pragma unroll
-        for (int kt = 0; kt < NKB; ++kt)
+        for (int kt = 0; kt < NKB; ++kt) ck[kt] = p.c;
+        if constexpr (FP8) {
+            const kconst_f32* ksc = (const kconst_f32*)(p.ksc + (long long)bh * p.nbk);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+            for (int kt = 0; kt < NKB; ++kt) ck[kt] = cq * ksc[min(kb + 32 * kt, L - 1) / p.bk];
+        }
+        float mx;
+        if constexpr (FP8) {
+            mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < NKB; ++kt) {
+                float m = sacc[kt][0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) m = fmaxf(m, sacc[kt][r]);
+                mx = fmaxf(mx, m * ck[kt]);
+            }
+        } else {
+            mx = sacc[0][0];
+#pragma unroll
+            for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+        }
         // running max mc in scaled log2 units (-inf while no key is seen);
         // O and l are rescaled only in waves where some row's max moved
-        const float cand = pair_max(mx) * p.c;
+        const float cand = FP8 ? pair_max(mx) : pair_max(mx) * p.c;
         const bool bump = cand > mc;
         const float alpha = bump ? __builtin_amdgcn_exp2f(mc - cand) : 1.f;
         mc = bump ? cand : mc;
@@ -751,7 +863,7 @@ void fa_fwd_h_kernel(Params p) {
                 float pe[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * ps + e], p.c, -ref));
+                    pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * ps + e], FP8 ? ck[kt] : p.c, -ref));
                     lsum += pe[e];
                 }
                 pf[kt][ps] = Ty<T>::cvt(pe);
@@ -891,6 +1003,9 @@ inline Params make_params(const void* q, const void* k, const void* v, void* o, 
     p.remap = (BH % 8 == 0) ? 1 : 0;
     p.c = scale * kLog2e;
     p.scale = scale;
+    p.qsc = nullptr;
+    p.ksc = nullptr;
+    p.bq = p.bk = p.nbq = p.nbk = 1;
     return p;
 }
 
@@ -903,7 +1018,8 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     const Params p = make_params(q, k, v, o, lse, BH, L, scale, t.br);
     const long long grid = (long long)BH * p.Tr;
     if constexpr (sizeof(T) == 2) {
-        hipLaunchKernelGGL((fa_fwd_h_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(HCfg<D>::NW * 64), 0, stream, p);
+        hipLaunchKernelGGL((fa_fwd_h_kernel<T, D, CAUSAL, false>), dim3((unsigned)grid), dim3(HCfg<D>::NW * 64), 0,
+                           stream, p);
     } else {
         using Ch = F32Choice<T, D>;
         hipLaunchKernelGGL((fa_fwd_f32_kernel<float, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>), dim3((unsigned)grid),
@@ -939,7 +1055,44 @@ int check_args(int B, int H, int L, int d, int causal, int dtype) {
     return FA_OK;
 }
 
+// FP8 scores: Q and K as E4M3 codes with block scales, V and O in T
+template <class T, int D, bool CAUSAL>
+int launch_fp8(const Params& p, hipStream_t stream) {
+    const long long grid = (long long)p.BH * p.Tr;
+    hipLaunchKernelGGL((fa_fwd_h_kernel<T, D, CAUSAL, true>), dim3((unsigned)grid), dim3(HCfg<D, true>::NW * 64), 0,
+                       stream, p);
+    return launch_status();
+}
+
+template <class T>
+int launch_fp8_t(const Params& p, int d, int causal, hipStream_t stream) {
+    if (d == 64) return causal ? launch_fp8<T, 64, true>(p, stream) : launch_fp8<T, 64, false>(p, stream);
+    return causal ? launch_fp8<T, 128, true>(p, stream) : launch_fp8<T, 128, false>(p, stream);
+}
+
 }  // namespace
+
+extern "C" int fa_fwd_fp8(const void* q8, const void* k8, const float* q_scale, const float* k_scale, const void* v,
+                          void* o, float* lse, int B, int H, int L, int d, float scale, int causal, int dtype,
+                          int block_q, int block_k, hipStream_t stream) {
+    if (!q8 || !k8 || !q_scale || !k_scale || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (block_q < 1 || block_k < 32 || block_k % 32 != 0) return FA_ERR_INVALID_ARG;
+    if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;             // V and O are 16-bit here
+    const int rc = check_args(B, H, L, d, causal, dtype);
+    if (rc != FA_OK) return rc;
+    if (((uintptr_t)q8 | (uintptr_t)k8 | (uintptr_t)v | (uintptr_t)o) % 16 != 0 ||
+        ((uintptr_t)lse | (uintptr_t)q_scale | (uintptr_t)k_scale) % 4 != 0)
+        return FA_ERR_ALIGN;
+    Params p = make_params(q8, k8, v, o, lse, B * H, L, scale, HCfg<128, true>::BR);
+    p.qsc = q_scale;
+    p.ksc = k_scale;
+    p.bq = block_q;
+    p.bk = block_k;
+    p.nbq = (L + block_q - 1) / block_q;
+    p.nbk = (L + block_k - 1) / block_k;
+    return dtype == FA_BF16 ? launch_fp8_t<__bf16>(p, d, causal, stream) : launch_fp8_t<_Float16>(p, d, causal, stream);
+}
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int L,
                       int d, float scale, int causal, int dtype, hipStream_t stream) {

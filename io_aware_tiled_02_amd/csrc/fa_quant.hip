@@ -1,0 +1,92 @@
+// FP8 (E4M3) block quantisation of Q or K for the FP8 forward pass, gfx950.
+//
+// "FlashAttention 深度解析", third article (FlashAttention-3), section 2.3:
+// Q and K are cut into blocks and each block is scaled into the FP8 range on
+// its own, s = max|block| / FP8_MAX, codes = Quantize(block / s); the scores
+// are dequantised after the product with s_q * s_k.  E4M3 is the OCP 8-bit
+// format (bias 7, no infinities, largest finite value 448), which is what
+// gfx950's v_cvt_pk_fp8_f32 produces, rounding to nearest even.
+//
+// A block is `block` consecutive rows of one (batch, head), all d columns:
+// one contiguous span of the (B, H, L, d) tensor.  One workgroup per block
+// reads it twice, once for the maximum and once to convert (the second read
+// is served from cache: a block of 128 rows is 32 KB at d = 128), so the
+// kernel moves 2 + 1 bytes of HBM per element.  The arithmetic is float32:
+// s = amax / 448 and x / s are IEEE-rounded divisions, and the quotient is
+// clamped to +-448 before conversion (the conversion does not saturate; the
+// clamp only absorbs the rounding of s).
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace {
+
+using namespace fa_dev;
+
+constexpr float kE4M3Max = 448.f;
+
+template <class T>
+__global__ __launch_bounds__(256) void fa_quant_kernel(const char* x, unsigned char* x8, float* scales, int L,
+                                                       int d, int block, int nblk) {
+    const int b = blockIdx.x, bh = blockIdx.y;
+    const int r0 = b * block, r1 = min(r0 + block, L);
+    const long long e0 = ((long long)bh * L + r0) * d;
+    const int n8 = (r1 - r0) * d / 8;             // 16-byte input pieces of the block
+    const char* src = x + e0 * 2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    float amax = 0.f;
+    for (int i = tid; i < n8; i += 256) {
+        float v[8];
+        load_elems<T, 8>(src + (long long)i * 16, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    __shared__ float red[4];
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax > 0.f ? amax / kE4M3Max : 1.f;
+    if (tid == 0) scales[(long long)bh * nblk + b] = s;
+
+    unsigned char* dst = x8 + e0;
+    for (int i = tid; i < n8; i += 256) {
+        float v[8];
+        load_elems<T, 8>(src + (long long)i * 16, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = fminf(fmaxf(v[e] / s, -kE4M3Max), kE4M3Max);
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
+        st8(dst + (long long)i * 8, u32x2{(uint32_t)w0, (uint32_t)w1});
+    }
+}
+
+}  // namespace
+
+extern "C" int fa_quantize_fp8(const void* x, int dtype, int B, int H, int L, int d, int block, void* x8,
+                               float* scales, hipStream_t stream) {
+    if (!x || !x8 || !scales) return FA_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || L <= 0 || block < 1) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H > 65535) return FA_ERR_INVALID_ARG;
+    if (((uintptr_t)x | (uintptr_t)x8) % 16 != 0 || (uintptr_t)scales % 4 != 0) return FA_ERR_ALIGN;
+    const int nblk = (L + block - 1) / block;
+    const dim3 grid((unsigned)nblk, (unsigned)(B * H));
+    if (dtype == FA_BF16)
+        hipLaunchKernelGGL((fa_quant_kernel<__bf16>), grid, dim3(256), 0, stream, static_cast<const char*>(x),
+                           static_cast<unsigned char*>(x8), scales, L, d, block, nblk);
+    else
+        hipLaunchKernelGGL((fa_quant_kernel<_Float16>), grid, dim3(256), 0, stream, static_cast<const char*>(x),
+                           static_cast<unsigned char*>(x8), scales, L, d, block, nblk);
+    return fa_detail::launch_status();
+}

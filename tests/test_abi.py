@@ -161,3 +161,57 @@ def test_bwd_argument_errors(kw, want):
 def test_bwd_workspace_size():
     assert fa.fa_bwd_workspace_bytes(1, 2, 100) == 1024      # 200 floats -> 800 B -> 1024
     assert fa.fa_bwd_workspace_bytes(0, 2, 100) == 0
+
+
+# ---- FP8 entry points ------------------------------------------------------------
+
+def _qz(**kw):
+    a = dict(x=A, dtype=2, B=1, H=2, L=100, d=128, block=64, x8=A, sc=A, stream=0)
+    a.update(kw)
+    return fa.fa_quantize_fp8(a["x"], a["dtype"], a["B"], a["H"], a["L"], a["d"], a["block"], a["x8"], a["sc"],
+                              a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=0), fa.FA_ERR_INVALID_ARG),
+    (dict(sc=0), fa.FA_ERR_INVALID_ARG),
+    (dict(L=0), fa.FA_ERR_INVALID_ARG),
+    (dict(block=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=300, H=300), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED),     # 16-bit inputs only
+    (dict(x=A + 8), fa.FA_ERR_ALIGN),
+    (dict(x8=A + 4), fa.FA_ERR_ALIGN),
+    (dict(sc=A + 2), fa.FA_ERR_ALIGN),
+])
+def test_quantize_fp8_argument_errors(kw, want):
+    assert _qz(**kw) == want
+
+
+def _f8(**kw):
+    a = dict(q8=A, k8=A, sq=A, sk=A, v=A, o=A, lse=A, B=1, H=2, L=100, d=128, scale=0.1, causal=0, dtype=2,
+             bq=64, bk=64, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_fp8(a["q8"], a["k8"], a["sq"], a["sk"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["L"],
+                         a["d"], a["scale"], a["causal"], a["dtype"], a["bq"], a["bk"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q8=0), fa.FA_ERR_INVALID_ARG),
+    (dict(sk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(L=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(bq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(bk=16), fa.FA_ERR_INVALID_ARG),       # key blocks are whole 32-key MFMA blocks
+    (dict(bk=48), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED),     # V and O are 16-bit
+    (dict(k8=A + 8), fa.FA_ERR_ALIGN),
+    (dict(o=A + 2), fa.FA_ERR_ALIGN),
+    (dict(sq=A + 1), fa.FA_ERR_ALIGN),
+])
+def test_fwd_fp8_argument_errors(kw, want):
+    assert _f8(**kw) == want
