@@ -43,14 +43,15 @@ def kernel_digest() -> str:
     return h.hexdigest()
 
 
-def traffic_for(workload_index: int):
-    """Measured HBM bytes per launch, if the counters were taken on this exact kernel source."""
+def traffic_for(workload):
+    """Measured HBM bytes per launch of the workload's attention kernel (key: the
+    workload index, or 'fp8'), if the counters were taken on this exact kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
     if rec.get("kernel_source_sha256") != kernel_digest():
         return None
-    w = rec.get("workloads", {}).get(str(workload_index))
+    w = rec.get("workloads", {}).get(str(workload))
     if not w:
         return None
     return w["hbm_bytes_per_launch"]
@@ -417,7 +418,7 @@ def bench_fp8(args, torch, fa, cfg):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": tflops_attn / peak,
-            "traffic": None,
+            "traffic": traffic_for("fp8") if cfg is gen.FP8[0] else None,
             "kernel": "fa_fwd_h_kernel (FP8 scores)",
             "per_launch_flops": cfg.flops,
             "avg_launch_ms": ms_attn,

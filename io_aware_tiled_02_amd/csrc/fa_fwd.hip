@@ -470,8 +470,10 @@ struct HCfg {
     static constexpr int LPWK = TILEK / 1024 / NW;  // ... per K tile
     static_assert(LPWK >= 1 && LPWK * NW * 1024 == TILEK, "tile must split into 1 KB pieces per wave");
     static_assert(LPW >= 1 && LPW * NW * 1024 == TILE, "tile must split into 1 KB pieces per wave");
-    // LDS: K stage 0, K stage 1, V stage 0, V stage 1
-    static constexpr int BYTES = 2 * TILEK + 2 * TILE;
+    // LDS: K stage 0, K stage 1, V stage 0, V stage 1; FP8 adds four 256-byte
+    // slots for the K tiles' block scales
+    static constexpr int SCOFF = 2 * TILEK + 2 * TILE;
+    static constexpr int BYTES = SCOFF + (FP8 ? 4 * 256 : 0);
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -486,7 +488,6 @@ struct K8Layout {
 };
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(4))) const float kconst_f32;   // read through the scalar cache
 
 // S^T += K Q^T over 64 d-values with E4M3 codes: the K row chunks (a0, a1)
 // and Q row chunks (b0, b1) hold 32 consecutive d-values of the lane's
@@ -497,6 +498,20 @@ __device__ inline f32x16 mma_e4m3(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16
     const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// LDS-DMA of one dword per lane: lane l's 4 bytes land at lds_base + 4l
+// (the same explicit-wait contract as dma16).
+__device__ inline void dma4(i32x4 rsrc, int voff, unsigned lds_base) {
+    int saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_base), "v"(voff), "s"(rsrc)
+        : "memory");
+}
+
 template <class F>
 __device__ inline f32x16 mma_e4m3(F a0, F a1, F b0, F b1, f32x16 c) {
     return mma_e4m3(__builtin_bit_cast(u32x4, a0), __builtin_bit_cast(u32x4, a1), __builtin_bit_cast(u32x4, b0),
@@ -619,7 +634,20 @@ void fa_fwd_h_kernel(Params p) {
     auto kdma_off = [&](int x, int hi) { return (kd0 ^ (x * 0x440)) + hi * 4096 * LPWK; };
     auto vdma_off = [&](int x, int hi) { return vd0 + 1024 * x + hi * 4096 * LPW; };
     const unsigned lds0 = (unsigned)(unsigned long long)(lds_char*)smem;
+    // FP8: the block scales of K tile t's NKB sub-tiles go to LDS slot t & 3
+    // (lane kt fetches sub-tile kt's; the slot is read in X(t), so it must
+    // outlive the stage of K_t by one phase: four slots)
+    i32x4 ksrs = i32x4{0, 0, 0, 0};
+    if constexpr (FP8) ksrs = buffer_rsrc(p.ksc + (long long)bh * p.nbk, p.nbk * 4);
+    auto issue_ksc = [&](int t) {
+        if constexpr (FP8) {
+            const int kt = lane < NKB ? lane : 0;
+            const int idx = min(t * BC + 32 * kt, L - 1) / p.bk;
+            dma4(ksrs, idx * 4, __builtin_amdgcn_readfirstlane(lds0 + Cf::SCOFF + (t & 3) * 256));
+        }
+    };
     auto issue_k2 = [&](int j) {
+        issue_ksc(j);
         const unsigned dst = lds0 + (j & 1) * TILEK + 1024 * wq * LPWK;
 #pragma unroll
         for (int x = 0; x < LPWK; ++x) {
@@ -662,7 +690,7 @@ void fa_fwd_h_kernel(Params p) {
     // waits for them at the end of its X(t) (phase 2t+1); the barrier there
     // publishes the stages, which are first read in phase 2t+2.
     const bool feeder = group == 0;
-    constexpr int NPIECE = 2 * LPWK + 2 * LPW;    // DMA instructions per wave for K_{t+1}, V_t
+    constexpr int NPIECE = 2 * LPWK + 2 * LPW + (FP8 ? 1 : 0);   // DMA instructions per wave for K_{t+1}, V_t
     auto dma_piece = [&](int t, int n) {          // n-th instruction of K_{t+1}, V_t
         const int hi = n & 1;
         // the descriptors move to the tile, so the per-lane offsets are loop-invariant
@@ -673,6 +701,8 @@ void fa_fwd_h_kernel(Params p) {
                 dma16(buffer_rsrc_at(kh, L * PK, (t + 1) * TILEK), kdma_off(x, hi),
                       __builtin_amdgcn_readfirstlane(dst));
             }
+        } else if (FP8 && n == NPIECE - 1) {
+            if (t + 1 < ntiles) issue_ksc(t + 1);
         } else {
             const int x = (n - 2 * LPWK) >> 1;
             const unsigned dst = lds0 + 2 * TILEK + (t & 1) * TILE + 1024 * (wq * LPW + x) + hi * 4096 * LPW;
@@ -821,9 +851,9 @@ void fa_fwd_h_kernel(Params p) {
 #pragma unroll
         for (int kt = 0; kt < NKB; ++kt) ck[kt] = p.c;
         if constexpr (FP8) {
-            const kconst_f32* ksc = (const kconst_f32*)(p.ksc + (long long)bh * p.nbk);
+            const float* ks = reinterpret_cast<const float*>(smem + Cf::SCOFF + (j & 3) * 256);
 #pragma unroll
-            for (int kt = 0; kt < NKB; ++kt) ck[kt] = cq * ksc[min(kb + 32 * kt, L - 1) / p.bk];
+            for (int kt = 0; kt < NKB; ++kt) ck[kt] = cq * ks[kt];
         }
         float mx;
         if constexpr (FP8) {

@@ -9,9 +9,9 @@
 //
 // A block is `block` consecutive rows of one (batch, head), all d columns:
 // one contiguous span of the (B, H, L, d) tensor.  One workgroup per block
-// reads it twice, once for the maximum and once to convert (the second read
-// is served from cache: a block of 128 rows is 32 KB at d = 128), so the
-// kernel moves 2 + 1 bytes of HBM per element.  The arithmetic is float32:
+// loads it into registers, reduces the maximum and converts what it holds,
+// so the kernel moves 2 + 1 bytes of HBM per element (blocks beyond 16K
+// elements are read a second time instead of held).  The arithmetic is float32:
 // s = amax / 448 and x / s are IEEE-rounded divisions, and the quotient is
 // clamped to +-448 before conversion (the conversion does not saturate; the
 // clamp only absorbs the rounding of s).
@@ -30,6 +30,34 @@ using namespace fa_dev;
 
 constexpr float kE4M3Max = 448.f;
 
+// Pieces (16 bytes, 8 elements) per thread kept in registers between the
+// two passes: blocks up to 256 * kKeep pieces (128 rows at d = 128) read HBM
+// once; larger blocks read it twice.
+constexpr int kKeep = 8;
+
+template <class T>
+__device__ inline void quant_store(const u32x4 raw, float s, unsigned char* dst) {
+    float v[8];
+    load_elems<T, 8>(reinterpret_cast<const char*>(&raw), v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = fminf(fmaxf(v[e] / s, -kE4M3Max), kE4M3Max);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
+    st8(dst, u32x2{(uint32_t)w0, (uint32_t)w1});
+}
+
+template <class T>
+__device__ inline float piece_amax(const u32x4 raw) {
+    float v[8];
+    load_elems<T, 8>(reinterpret_cast<const char*>(&raw), v);
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    return m;
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void fa_quant_kernel(const char* x, unsigned char* x8, float* scales, int L,
                                                        int d, int block, int nblk) {
@@ -38,14 +66,22 @@ __global__ __launch_bounds__(256) void fa_quant_kernel(const char* x, unsigned c
     const long long e0 = ((long long)bh * L + r0) * d;
     const int n8 = (r1 - r0) * d / 8;             // 16-byte input pieces of the block
     const char* src = x + e0 * 2;
+    unsigned char* dst = x8 + e0;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool keep = n8 <= 256 * kKeep;
 
+    u32x4 held[kKeep];
     float amax = 0.f;
-    for (int i = tid; i < n8; i += 256) {
-        float v[8];
-        load_elems<T, 8>(src + (long long)i * 16, v);
+    if (keep) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+        for (int p = 0; p < kKeep; ++p) {
+            const int i = tid + 256 * p;
+            held[p] = i < n8 ? ld16(src + (long long)i * 16) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int p = 0; p < kKeep; ++p) amax = fmaxf(amax, piece_amax<T>(held[p]));
+    } else {
+        for (int i = tid; i < n8; i += 256) amax = fmaxf(amax, piece_amax<T>(ld16(src + (long long)i * 16)));
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
@@ -56,17 +92,14 @@ __global__ __launch_bounds__(256) void fa_quant_kernel(const char* x, unsigned c
     const float s = amax > 0.f ? amax / kE4M3Max : 1.f;
     if (tid == 0) scales[(long long)bh * nblk + b] = s;
 
-    unsigned char* dst = x8 + e0;
-    for (int i = tid; i < n8; i += 256) {
-        float v[8];
-        load_elems<T, 8>(src + (long long)i * 16, v);
+    if (keep) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = fminf(fmaxf(v[e] / s, -kE4M3Max), kE4M3Max);
-        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
-        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
-        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
-        st8(dst + (long long)i * 8, u32x2{(uint32_t)w0, (uint32_t)w1});
+        for (int p = 0; p < kKeep; ++p) {
+            const int i = tid + 256 * p;
+            if (i < n8) quant_store<T>(held[p], s, dst + (long long)i * 8);
+        }
+    } else {
+        for (int i = tid; i < n8; i += 256) quant_store<T>(ld16(src + (long long)i * 16), s, dst + (long long)i * 8);
     }
 }
 
