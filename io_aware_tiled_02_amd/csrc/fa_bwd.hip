@@ -91,6 +91,21 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p, long long 
     if (valid && (lane & 15) == 0) p.dvec[row] = acc;
 }
 
+// Row layout of the streamed tiles.  Each tile is read two ways: as rows
+// (16 lanes of a ds_read_b128 pass read one chunk of 16 different rows) and
+// transposed (32 lanes of a ds_read_b64_tr_b16 pass read 4 consecutive rows,
+// 4 chunks each).  Chunk c of row r is stored at c ^ fb(r): fb is a bijection
+// on the 16 rows that share a bank position (row reads conflict-free), and
+// its bit 2 and up (which 4-chunk group a row's chunks land in) differs
+// between the rows of one 4-row step that share a bank position (transposing
+// reads conflict-free).  d = 128 (rows of 256 bytes, all rows at bank 0):
+// fb = 4 (r mod 4) + (r / 4 mod 4).  d = 64 (two rows per 256 bytes):
+// fb = 4 (r / 2 mod 2) + (r / 4 mod 4).
+template <int D>
+__device__ inline int fb(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
 // Per-lane LDS offsets shared by both kernels, all derived from two base
 // values by XOR with constants (so only the bases stay live across a loop).
 //  row(s)    : the 16-byte chunk (2s + hf) of row l32 (A operand of a row
@@ -100,24 +115,23 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p, long long 
 //  tr(dt,hi) : transposing reads (A operand d x rows): lane 16g+4e+q reads
 //              row 4*(g>>1) + e (+8 for hi) of a 16-row step, d columns of
 //              chunk 4dt + 2(g&1) + (q>>1), half (q&1).  dt flips chunk bits
-//              2.. (offset bits 6..); the +8 rows flip one row bit and the
-//              swizzle bit it drives.  Rows 0..15 and 16..31 of a 32-row
-//              group share the swizzle (period 16).
+//              2.. (offset bits 6..); the +8 rows flip one row bit and fb's
+//              bit 1.  Rows 0..15 and 16..31 of a 32-row group share the
+//              swizzle (period 16).
 template <int D>
 struct Offs {
-    static constexpr int kTrHi = D == 128 ? 0x880 : 0x440;
+    static constexpr int kTrHi = D == 128 ? 0x820 : 0x420;
     int row0, tr0;
     __device__ int row(int s) const { return row0 ^ (s << 5); }
     __device__ int tr(int dt, int hi) const { return tr0 ^ (dt << 6) ^ (hi ? kTrHi : 0); }
     __device__ void init(int lane) {
-        using Lay = HLayout<D>;
         constexpr int P = 2 * D;
         const int l32 = lane & 31, hf = lane >> 5;
-        row0 = l32 * P + ((hf ^ Lay::fk(l32)) << 4);
+        row0 = l32 * P + ((hf ^ fb<D>(l32)) << 4);
         const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
         const int r = 4 * (g >> 1) + e;
         const int c = 2 * (g & 1) + (q >> 1);
-        tr0 = r * P + ((c ^ Lay::fk(r)) << 4) + 8 * (q & 1);
+        tr0 = r * P + ((c ^ fb<D>(r)) << 4) + 8 * (q & 1);
     }
     // The same offsets, opaque to the optimiser: called inside a loop body, the
     // derived offsets are recomputed there (a few XORs) instead of being
@@ -130,16 +144,19 @@ struct Offs {
 };
 
 // DMA: piece n of a tile (1 KB, lane l its 16 bytes at LDS offset 1024n+16l)
-// holds global chunk slot ^ fk(row) of that row.  For the PPW pieces of one
-// wave, piece wave*PPW + x reads at dma_goff(wave*PPW) ^ (x * 0x440): x adds
-// 4 rows (bit 10) and flips swizzle bit 2 of the chunk (bit 6).
+// holds global chunk slot ^ fb(row) of that row.  For the PPW pieces of one
+// wave, piece wave*PPW + x reads at dma_goff(wave*PPW) ^ (x * kPieceX): x
+// adds 1024 bytes of rows (bit 10 up) and flips fb bits the piece's rows
+// determine (chunk bit 0 at d = 128, bit 1 at d = 64).
+template <int D>
+constexpr int kPieceX = D == 128 ? 0x410 : 0x420;
+
 template <int D>
 __device__ inline int dma_goff(int n, int lane) {
-    using Lay = HLayout<D>;
     constexpr int P = 2 * D;
     const int o = 1024 * n + 16 * lane;
     const int r = o / P, slot = (o % P) >> 4;
-    return r * P + ((slot ^ Lay::fk(r)) << 4);
+    return r * P + ((slot ^ fb<D>(r)) << 4);
 }
 
 // A operand read transposed from a row-major tile at row offset rowb (bytes).
@@ -213,8 +230,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int x = 0; x < PPW; ++x) {
             const unsigned dst = lds0 + (t & 1) * TILE + 1024 * (wave * PPW + x);
-            dma16(kr, g0 ^ (x * 0x440), __builtin_amdgcn_readfirstlane(dst));
-            dma16(vr, g0 ^ (x * 0x440), __builtin_amdgcn_readfirstlane(dst + 2 * TILE));
+            dma16(kr, g0 ^ (x * kPieceX<D>), __builtin_amdgcn_readfirstlane(dst));
+            dma16(vr, g0 ^ (x * kPieceX<D>), __builtin_amdgcn_readfirstlane(dst + 2 * TILE));
         }
     };
 
@@ -336,8 +353,8 @@ __device__ __attribute__((always_inline)) inline void fa_bwd_dkdv_body(const Bwd
 #pragma unroll
         for (int x = 0; x < PPW; ++x) {
             const unsigned dst = lds0 + (t & 1) * TILE + 1024 * (wave * PPW + x);
-            dma16(qr, g0 ^ (x * 0x440), __builtin_amdgcn_readfirstlane(dst));
-            dma16(gr, g0 ^ (x * 0x440), __builtin_amdgcn_readfirstlane(dst + 2 * TILE));
+            dma16(qr, g0 ^ (x * kPieceX<D>), __builtin_amdgcn_readfirstlane(dst));
+            dma16(gr, g0 ^ (x * kPieceX<D>), __builtin_amdgcn_readfirstlane(dst + 2 * TILE));
         }
     };
     // row statistics of tile t (wave 0): lse in base-2 units (+inf past L, so
