@@ -196,8 +196,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int L);
  *           fa_bwd_workspace_bytes(B, H, L) bytes, 256-byte aligned; it holds
  *           D = rowsum(dO (.) O) until the kernels on `stream` have read it.
  * Ownership, asynchrony and errors as for fa_fwd (all tensors 16-byte
- * aligned, lse 4-byte aligned); B*H > 65535 or L*d*2 >= 2^31 returns
- * FA_ERR_INVALID_ARG.
+ * aligned, lse 4-byte aligned); B*H*ceil(L/128) > 2^31 - 1 or
+ * L*d*2 >= 2^31 returns FA_ERR_INVALID_ARG.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, int B, int H, int L, int d, float scale, int causal, int dtype,

@@ -181,6 +181,34 @@ __device__ inline void load_row_frags(const char* base, int row, int L, int hf, 
     for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(f[s]));
 }
 
+// Which (head, block of 128 rows) workgroup blockIdx.x owns, in a 1-D grid
+// of BH * nblk.  Workgroup ids are dealt round-robin to the 8 XCDs (id % 8);
+// when BH is a multiple of 8 each XCD gets whole heads, whose streamed tiles
+// then come through its own L2.  Causal: the blocks with the most work are
+// dispatched first, across all heads (heavy_last: the last block is the
+// heaviest, else the first).
+__device__ inline void bwd_tile(int nblk, int BH, bool causal, bool heavy_last, int& bh, int& blk) {
+    const int id = blockIdx.x;
+    int rank;                                    // position in dispatch order within the XCD's share
+    if (BH % 8 == 0) {
+        const int xcd = id & 7, s = id >> 3, hp = BH >> 3;
+        if (causal) {
+            rank = s / hp;
+            bh = xcd * hp + s % hp;
+        } else {
+            bh = xcd * hp + s / nblk;
+            rank = s % nblk;
+        }
+    } else if (causal) {
+        rank = id / BH;
+        bh = id % BH;
+    } else {
+        bh = id / nblk;
+        rank = id % nblk;
+    }
+    blk = causal && heavy_last ? nblk - 1 - rank : rank;
+}
+
 // ---- dQ: one workgroup per 128 queries ----
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -194,9 +222,9 @@ void fa_bwd_dq_kernel(BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
     const int L = p.L;
-    const int bh = blockIdx.y;
     // causal: the last query blocks see the most keys; dispatch them first
-    const int qb = CAUSAL ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    int bh, qb;
+    bwd_tile((L + 127) / 128, p.BH, CAUSAL, true, bh, qb);
     const int q0 = qb * 128;
     const int qw = q0 + 32 * wave;
     const int qend = min(q0 + 128, L);
@@ -323,8 +351,10 @@ __device__ __attribute__((always_inline)) inline void fa_bwd_dkdv_body(const Bwd
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
     const int L = p.L;
-    const int bh = blockIdx.y;
-    const int k0 = blockIdx.x * 128;
+    // causal: the first key blocks see the most queries; dispatch them first
+    int bh, kb;
+    bwd_tile((L + 127) / 128, p.BH, CAUSAL, false, bh, kb);
+    const int k0 = kb * 128;
     const int kw = k0 + 32 * wave;
     const int key = kw + l32;
     const long long head = (long long)bh * L * D;
@@ -499,7 +529,7 @@ int launch_bwd(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((fa_bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p, rows);
     int rc = fa_detail::launch_status();
     if (rc != FA_OK) return rc;
-    const dim3 grid((unsigned)((p.L + 127) / 128), (unsigned)p.BH);
+    const dim3 grid((unsigned)((long long)p.BH * ((p.L + 127) / 128)));
     hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
     rc = fa_detail::launch_status();
     if (rc != FA_OK) return rc;
@@ -531,7 +561,7 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-    if ((long long)B * H > 65535) return FA_ERR_INVALID_ARG;
+    if ((long long)B * H * ((L + 127) / 128) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;   // one grid dimension
     // per-head byte offsets go through 32-bit buffer descriptors
     if ((long long)L * d * 2 >= (1LL << 31)) return FA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||

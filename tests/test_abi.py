@@ -147,7 +147,7 @@ def _bw(**kw):
     (dict(causal=3), fa.FA_ERR_INVALID_ARG),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=0), fa.FA_ERR_UNSUPPORTED),     # no fp32 backward
-    (dict(B=300, H=300), fa.FA_ERR_INVALID_ARG),
+    (dict(B=65536, H=65536), fa.FA_ERR_INVALID_ARG),   # B*H*ceil(L/128) workgroups over one grid dimension
     (dict(L=1 << 23), fa.FA_ERR_INVALID_ARG),   # L*d*2 >= 2^31
     (dict(dq=A + 8), fa.FA_ERR_ALIGN),
     (dict(lse=A + 2), fa.FA_ERR_ALIGN),

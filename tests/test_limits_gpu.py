@@ -1,9 +1,9 @@
 """GPU parity at the size limits of each entry point.
 
-* grid limits: the forward pass puts (B*H, query tile) on one grid dimension
-  and takes B*H beyond 65535; the backward pass, split-K/V and the FP8
-  quantiser put B*H on the second grid dimension, whose limit (65535) they
-  accept exactly;
+* grid limits: the forward and backward passes put (B*H, row block) on one
+  grid dimension and take B*H beyond 65535; split-K/V and the FP8 quantiser
+  put B*H on the second grid dimension, whose limit (65535) they accept
+  exactly;
 * a long sequence: L = 65536 in one head, non-causal and causal, checked on
   sampled rows (the first, the last and rows across the range).
 Every case names itself before it touches the GPU.
@@ -55,14 +55,15 @@ def test_forward_long_sequence(dtype, d, causal):
     compare(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, dtype, f"L={L}")
 
 
-def test_backward_65535_heads():
-    shape = (5, 13107, 3, 64)                     # B*H = 65535
-    say("[limits] fa_bwd B*H=65535 L=3 d=64 causal=1")
+@pytest.mark.parametrize("causal", [0, 1])
+def test_backward_beyond_65535_heads(causal):
+    shape = (3, 21846, 3, 64)                     # B*H = 65538
+    say(f"[limits] fa_bwd B*H=65538 L=3 d=64 causal={causal}")
     q, k, v = _qkv(shape, 63)
     g = gen.fill(gen.BF16, shape, 63, 3)
-    got = run_bwd(q, k, v, g, gen.BF16, 0.125, 1)
-    ref = oracle.bwd(q, k, v, g, gen.BF16, 0.125, 1)
-    compare_grads(got, ref, "B*H=65535")
+    got = run_bwd(q, k, v, g, gen.BF16, 0.125, causal)
+    ref = oracle.bwd(q, k, v, g, gen.BF16, 0.125, causal)
+    compare_grads(got, ref, "B*H=65538")
 
 
 def test_splitkv_65535_heads():
