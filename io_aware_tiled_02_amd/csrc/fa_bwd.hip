@@ -24,8 +24,9 @@
 //  So dK/dV and dQ are each reduced inside one workgroup; the price is that
 //  S and dP are formed twice (seven 32x32-tile products per block instead of
 //  five).  Tiles arrive by LDS-DMA into double-buffered stages, rows
-//  XOR-swizzled (the same row layout serves the row reads and the
-//  transposing reads).
+//  XOR-swizzled so that both the row reads and the transposing reads are
+//  free of bank conflicts.  Both kernels run a 1-D grid: heads grouped per
+//  XCD, and causal blocks in heavy-first order across all heads.
 
 #include <hip/hip_runtime.h>
 
