@@ -415,12 +415,29 @@ __device__ __attribute__((always_inline)) inline void fa_bwd_dkdv_body(const Bwd
         f32x16 st, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[r] = dp[r] = 0.f;
+        // Q and dO row operands are read two steps ahead of their MFMAs, the
+        // transposed ones of the dV/dK products one step ahead; the scheduling
+        // groups keep that order (the registers allow it at two waves per SIMD)
+        frag qa3[3], ga3[3];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            qa3[s] = __builtin_bit_cast(frag, ld16(qs + qt * 32 * P + o.row(s)));
+            ga3[s] = __builtin_bit_cast(frag, ld16(gs + qt * 32 * P + o.row(s)));
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const frag a = __builtin_bit_cast(frag, ld16(qs + qt * 32 * P + o.row(s)));
-            const frag b = __builtin_bit_cast(frag, ld16(gs + qt * 32 * P + o.row(s)));
-            st = Ty<T>::mma(a, kf[s], st);
-            dp = Ty<T>::mma(b, vf[s], dp);
+            if (s + 2 < D / 16) {
+                qa3[(s + 2) % 3] = __builtin_bit_cast(frag, ld16(qs + qt * 32 * P + o.row(s + 2)));
+                ga3[(s + 2) % 3] = __builtin_bit_cast(frag, ld16(gs + qt * 32 * P + o.row(s + 2)));
+            }
+            st = Ty<T>::mma(qa3[s % 3], kf[s], st);
+            dp = Ty<T>::mma(ga3[s % 3], vf[s], dp);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
         // register r holds query t*64 + 32qt + 8(r/4) + 4hf + r%4 of key `key`.
         // P and dS are formed and consumed in two halves (registers 8ps..8ps+7,
@@ -447,12 +464,23 @@ __device__ __attribute__((always_inline)) inline void fa_bwd_dkdv_body(const Bwd
             }
             const frag pf = Ty<T>::cvt(pr), sf = Ty<T>::cvt(ds);
             const int rowb = (qt * 32 + 16 * ps) * P;
+            frag tg[2], tq[2];
+            tg[0] = tr_frag<T>(gsl + rowb, o.tr(0, 0), o.tr(0, 1));
+            tq[0] = tr_frag<T>(qsl + rowb, o.tr(0, 0), o.tr(0, 1));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                const frag ga = tr_frag<T>(gsl + rowb, o.tr(dt, 0), o.tr(dt, 1));
-                dva[dt] = Ty<T>::mma(ga, pf, dva[dt]);
-                const frag qa = tr_frag<T>(qsl + rowb, o.tr(dt, 0), o.tr(dt, 1));
-                dka[dt] = Ty<T>::mma(qa, sf, dka[dt]);
+                if (dt + 1 < D / 32) {
+                    tg[(dt + 1) & 1] = tr_frag<T>(gsl + rowb, o.tr(dt + 1, 0), o.tr(dt + 1, 1));
+                    tq[(dt + 1) & 1] = tr_frag<T>(qsl + rowb, o.tr(dt + 1, 0), o.tr(dt + 1, 1));
+                }
+                dva[dt] = Ty<T>::mma(tg[dt & 1], pf, dva[dt]);
+                dka[dt] = Ty<T>::mma(tq[dt & 1], sf, dka[dt]);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
