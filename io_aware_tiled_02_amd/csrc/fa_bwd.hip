@@ -278,12 +278,28 @@ void fa_bwd_dq_kernel(BwdParams p) {
             f32x16 st, dpt;
 #pragma unroll
             for (int r = 0; r < 16; ++r) st[r] = dpt[r] = 0.f;
+            // K and V row operands are read two steps ahead of their MFMAs,
+            // the transposed K operands of the dQ products likewise
+            frag ka3[3], va3[3];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                ka3[s] = __builtin_bit_cast(frag, ld16(ks + kt * 32 * P + o.row(s)));
+                va3[s] = __builtin_bit_cast(frag, ld16(vs + kt * 32 * P + o.row(s)));
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < D / 16; ++s) {
-                const frag a = __builtin_bit_cast(frag, ld16(ks + kt * 32 * P + o.row(s)));
-                const frag b = __builtin_bit_cast(frag, ld16(vs + kt * 32 * P + o.row(s)));
-                st = Ty<T>::mma(a, qf[s], st);
-                dpt = Ty<T>::mma(b, gf[s], dpt);
+                if (s + 2 < D / 16) {
+                    ka3[(s + 2) % 3] = __builtin_bit_cast(frag, ld16(ks + kt * 32 * P + o.row(s + 2)));
+                    va3[(s + 2) % 3] = __builtin_bit_cast(frag, ld16(vs + kt * 32 * P + o.row(s + 2)));
+                }
+                st = Ty<T>::mma(ka3[s % 3], qf[s], st);
+                dpt = Ty<T>::mma(va3[s % 3], gf[s], dpt);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // register r holds key t*64 + 32kt + 4hf + 8(r/4) + r%4
             const int lim = last - t * 64 - 32 * kt - 4 * hf;
@@ -295,14 +311,24 @@ void fa_bwd_dq_kernel(BwdParams p) {
                 ds[r] = pr * (dpt[r] - dval);
             }
             const frag d0 = Ty<T>::cvt(ds), d1 = Ty<T>::cvt(ds + 8);
+            constexpr int NI = D / 16;            // (ps, dt) = (i / (D/32), i % (D/32))
+            frag ta[3];
 #pragma unroll
-            for (int ps = 0; ps < 2; ++ps) {
-                const int rowb = (kt * 32 + 16 * ps) * P;
+            for (int i = 0; i < 2; ++i)
+                ta[i] = tr_frag<T>(ksl + (kt * 32 + 16 * (i / (D / 32))) * P, o.tr(i % (D / 32), 0),
+                                   o.tr(i % (D / 32), 1));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const frag a = tr_frag<T>(ksl + rowb, o.tr(dt, 0), o.tr(dt, 1));
-                    acc[dt] = Ty<T>::mma(a, ps ? d1 : d0, acc[dt]);
+            for (int i = 0; i < NI; ++i) {
+                if (i + 2 < NI) {
+                    const int j = i + 2;
+                    ta[j % 3] = tr_frag<T>(ksl + (kt * 32 + 16 * (j / (D / 32))) * P, o.tr(j % (D / 32), 0),
+                                           o.tr(j % (D / 32), 1));
                 }
+                acc[i % (D / 32)] = Ty<T>::mma(ta[i % 3], i / (D / 32) ? d1 : d0, acc[i % (D / 32)]);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
