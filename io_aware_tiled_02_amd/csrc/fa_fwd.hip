@@ -1003,9 +1003,10 @@ struct Tiling {
     int br, bc;
 };
 
-// Tile shapes: 16-bit types use fa_fwd_h_kernel (4 waves x 32 query rows,
-// 64-key tiles); fp32 uses fa_fwd_f32_kernel (64-key tiles at d = 64, 32-key
-// tiles at d = 128 for the LDS budget).
+// Tile shapes: 16-bit types (and FP8 scores) use fa_fwd_h_kernel (8 waves x
+// 32 query rows, 128-key tiles); fp32 uses fa_fwd_f32_kernel (4 waves x 32
+// query rows; 64-key tiles at d = 64, 32-key tiles at d = 128 for the LDS
+// budget).
 template <class T, int D>
 struct F32Choice {
     static constexpr int NQB = 1, NW = 4, NKB = (D == 64 ? 2 : 1);
