@@ -435,7 +435,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the engine clock ramps up over the first ~0.1 s of load: 100 untimed steps
+    # (about 0.1 s of the bench workload) reach the steady-state rate
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="3",
                     help="workload index 0..4 (default 3); 'decode' (split-K/V decoding shape); "
                          "'bwd' / 'bwd-causal' (backward pass shapes); 'fp8' / 'fp8-causal' (FP8 forward)")
