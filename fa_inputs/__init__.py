@@ -20,12 +20,22 @@ Generator (its published definitions, restated):
   * value = sigma * z in float64, rounded to float32 (round-to-nearest-even),
     then, for the 16-bit types, rounded again to fp16 / bf16 (RNE).
 
+The floating-point steps (Box-Muller and the roundings) have one definition,
+the C library fa_inputs/libfa_gen.so (source fa_gen.c, declared in
+include/fa_gen.h, built with gcc by ``build()``): ``normal`` and ``fill`` call
+it.  It uses the C library's log, cos and sqrt; numpy's own log differs from
+it in the last bit for a fraction of arguments, so the normals are not
+recomputed in numpy.  The integer steps (SplitMix64 and the uniforms) are
+exact in both languages; they are also written out here in numpy (used to
+draw sampled rows) and checked against the C library by the tests.
+
 This is not torch.randn; values are i.i.d. N(0, sigma^2) up to the rounding.
 """
 from __future__ import annotations
 
+import ctypes
 import os
-from concurrent.futures import ThreadPoolExecutor
+import subprocess
 
 import numpy as np
 
@@ -39,7 +49,49 @@ _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _MIX1 = np.uint64(0xBF58476D1CE4E5B9)
 _MIX2 = np.uint64(0x94D049BB133111EB)
 _KEY_STREAM = np.uint64(0xD1B54A32D192ED03)
-_CHUNK = 1 << 20
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_HERE)
+_SRC = os.path.join(_HERE, "fa_gen.c")
+LIB_PATH = os.path.join(_HERE, "libfa_gen.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the generator with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+               "-I" + os.path.join(_ROOT, "include"), "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    """The loaded generator library (built on first use if missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build(force=True)
+        l = ctypes.CDLL(LIB_PATH)
+        vp, i, sz, u64, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint64, ctypes.c_double
+        l.fa_gen_key.argtypes = [u64, u64]
+        l.fa_gen_key.restype = u64
+        l.fa_gen_splitmix64.argtypes = [u64, u64]
+        l.fa_gen_splitmix64.restype = u64
+        l.fa_gen_fill.argtypes = [vp, i, sz, u64, u64, d]
+        l.fa_gen_fill.restype = i
+        l.fa_gen_fill_range.argtypes = [vp, i, sz, sz, u64, u64, d]
+        l.fa_gen_fill_range.restype = i
+        l.fa_gen_normal.argtypes = [vp, sz, sz, u64, u64, d]
+        l.fa_gen_normal.restype = i
+        l.fa_gen_f32_to_f16.argtypes = [vp, vp, sz]
+        l.fa_gen_f32_to_f16.restype = None
+        l.fa_gen_f32_to_bf16.argtypes = [vp, vp, sz]
+        l.fa_gen_f32_to_bf16.restype = None
+        _lib = l
+    return _lib
 
 
 def _key(seed: int, stream: int) -> np.uint64:
@@ -76,10 +128,11 @@ def uniform01(seed: int, stream: int, start: int, count: int) -> np.ndarray:
 
 def normal(seed: int, stream: int, count: int, sigma: float = 1.0, start: int = 0) -> np.ndarray:
     """sigma * N(0,1) in float64 for element counters start .. start+count-1."""
-    u = uniform01(seed, stream, 2 * start, 2 * count)
-    u1 = u[0::2]
-    u2 = u[1::2]
-    return sigma * (np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2))
+    out = np.empty(count, dtype=np.float64)
+    rc = lib().fa_gen_normal(out.ctypes.data, start, count, seed, stream, float(sigma))
+    if rc != 0:
+        raise RuntimeError(f"fa_gen_normal failed: {rc}")
+    return out
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -108,24 +161,9 @@ def fill(dtype: int, shape, seed: int, stream: int, sigma: float = 1.0) -> np.nd
         out = np.empty(n, dtype=np.uint16)
     else:
         raise ValueError(f"unknown dtype code {dtype}")
-    def work(s):
-        c = min(_CHUNK, n - s)
-        v32 = normal(seed, stream, c, sigma, start=s).astype(np.float32)
-        if dtype == F32:
-            out[s:s + c] = v32
-        elif dtype == F16:
-            out[s:s + c] = v32.astype(np.float16)
-        else:
-            out[s:s + c] = f32_to_bf16_bits(v32)
-
-    starts = range(0, n, _CHUNK)
-    if n > _CHUNK:
-        # chunks are independent (counter-based), so order does not matter
-        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
-            list(ex.map(work, starts))
-    else:
-        for s in starts:
-            work(s)
+    rc = lib().fa_gen_fill(out.ctypes.data, dtype, n, seed, stream, float(sigma))
+    if rc != 0:
+        raise RuntimeError(f"fa_gen_fill failed: {rc}")
     return out.reshape(shape)
 
 

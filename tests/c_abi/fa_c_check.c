@@ -6,8 +6,9 @@
  * With the argument "args" it only checks that bad arguments come back as
  * the documented status codes (no GPU needed).
  *
- * Inputs come from a SplitMix64 counter (uniform in [-2, 2)), rounded to the
- * storage type on the host.  Exit status 0 when every case meets its bar:
+ * Inputs come from the seeded C generator (include/fa_gen.h: N(0,1) values
+ * rounded to the storage type on the host), streams 0/1/2 for Q/K/V.  Exit
+ * status 0 when every case meets its bar:
  * 16-bit O max-abs <= 2e-2, mean-abs <= 2e-3, lse max-abs <= 1e-3; fp32 O and
  * lse within 1e-5 relative (to max|O| and max(1, max|lse|)).
  */
@@ -18,6 +19,7 @@
 #include <string.h>
 
 #include "fa.h"
+#include "fa_gen.h"
 #include "fa_oracle.h"
 
 #define HIP_OK(x)                                                          \
@@ -28,26 +30,6 @@
             exit(2);                                                       \
         }                                                                  \
     } while (0)
-
-static uint64_t splitmix64(uint64_t x) {
-    x += 0x9E3779B97F4A7C15ull;
-    x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
-    x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
-    return x ^ (x >> 31);
-}
-
-/* value i of stream s: uniform in [-2, 2) with 24 random bits */
-static float uval(uint64_t s, uint64_t i) {
-    return (float)((splitmix64(s * 0x100000000ull + i) >> 40) * (4.0 / 16777216.0) - 2.0);
-}
-
-/* float -> bfloat16 bits, round to nearest even (finite inputs) */
-static uint16_t to_bf16(float f) {
-    uint32_t u;
-    memcpy(&u, &f, 4);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
 
 static float bf16_to_float(uint16_t h) {
     uint32_t u = (uint32_t)h << 16;
@@ -62,10 +44,9 @@ static int run_case(int dtype, int B, int H, int L, int d, int causal, float sca
     void* host[3];
     for (int t = 0; t < 3; ++t) {
         host[t] = malloc(n * esz);
-        for (size_t i = 0; i < n; ++i) {
-            const float x = uval(seed * 3 + t, i);
-            if (dtype == FA_F32) ((float*)host[t])[i] = x;
-            else ((uint16_t*)host[t])[i] = to_bf16(x);
+        if (fa_gen_fill(host[t], dtype, n, seed, (uint64_t)t, 1.0) != 0) {
+            fprintf(stderr, "fa_gen_fill rejected the case\n");
+            return 1;
         }
     }
     void *q, *k, *v, *o;

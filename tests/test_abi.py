@@ -12,22 +12,33 @@ import io_aware_tiled_02_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    names = set()
-    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
-        text = open(h).read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(", text, flags=re.M):
-            names.add(m.group(1))
-    return names
+def _declared_functions(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return {m.group(1) for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(", text, flags=re.M)}
+
+
+def test_every_header_is_covered():
+    # fa.h: the attention library; fa_gen.h: the input generator library
+    assert sorted(os.path.basename(h) for h in glob.glob(os.path.join(ROOT, "include", "*.h"))) == \
+        ["fa.h", "fa_gen.h"]
 
 
 def test_library_exports_every_declared_function():
     lib = fa.load()
-    names = _declared_functions()
+    names = _declared_functions("fa.h")
     assert {"fa_fwd", "fa_strerror", "fa_last_hip_error", "fa_fwd_tiling"} <= names
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/fa.h but not exported"
+
+
+def test_generator_library_exports_every_declared_function():
+    import fa_inputs
+    lib = fa_inputs.lib()
+    names = _declared_functions("fa_gen.h")
+    assert {"fa_gen_fill", "fa_gen_fill_range", "fa_gen_normal", "fa_gen_splitmix64", "fa_gen_key"} <= names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/fa_gen.h but not exported"
 
 
 def test_strerror_total():
