@@ -30,6 +30,7 @@ PEAK_TFLOPS = {gen.BF16: 2516.6, gen.F16: 2516.6, gen.F32: 157.3}   # dense MFMA
 # the sources the forward kernel is compiled from (the traffic record is keyed to them)
 KERNEL_SRCS = [os.path.join(ROOT, "io_aware_tiled_02_amd", "csrc", n) for n in ("fa_fwd.hip", "fa_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_kernel.json")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_fa_fwd_kernel.json")
 
 
 def log(msg):
@@ -55,6 +56,26 @@ def traffic_for(workload):
     if not w:
         return None
     return w["hbm_bytes_per_launch"]
+
+
+def counters_for(workload, ms_per_launch):
+    """SQ-counter figures of the workload's attention kernel (rocprofv3 --pmc runs
+    made by --collect-counters), if they were taken on this exact kernel source;
+    with the achieved HBM rate of this run when the traffic record exists."""
+    if not os.path.exists(COUNTER_FILE):
+        return None
+    rec = json.load(open(COUNTER_FILE))
+    if rec.get("kernel_source_sha256") != kernel_digest():
+        return None
+    w = rec.get("workloads", {}).get(str(workload))
+    if not w:
+        return None
+    out = {k: w[k] for k in ("mfma_busy", "mfma_valu_coexec", "lds_busy", "lds_bank_conflict_cycles",
+                             "engine_clock_ghz", "duration_ms_under_counters", "summary") if k in w}
+    traffic = traffic_for(workload)
+    if traffic is not None and ms_per_launch:
+        out["hbm_gbps"] = traffic / (ms_per_launch * 1e-3) / 1e9
+    return out
 
 
 def cpu_baseline(cfg, q, k, v, target_s: float):
@@ -418,11 +439,12 @@ def bench_fp8(args, torch, fa, cfg):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": tflops_attn / peak,
-            "traffic": traffic_for("fp8") if cfg is gen.FP8[0] else None,
+            "traffic": traffic_for(args.workload),
             "kernel": "fa_fwd_h_kernel (FP8 scores)",
             "per_launch_flops": cfg.flops,
             "avg_launch_ms": ms_attn,
         },
+        "counters": counters_for(args.workload, ms_attn),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -443,6 +465,16 @@ def main():
                          "'bwd' / 'bwd-causal' (backward pass shapes); 'fp8' / 'fp8-causal' (FP8 forward)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU-baseline run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--collect-counters", action="store_true",
+                    help="run rocprofv3 (kernel trace, SQ counter passes, FETCH/WRITE_SIZE against a plain copy) "
+                         "on this workload as child processes; write the summaries and records under profiles/")
+    ap.add_argument("--summarize-counters", action="store_true",
+                    help="only the summary step of --collect-counters, from raw output already under --prof-dir")
+    ap.add_argument("--prof-dir", default=os.path.join(ROOT, "gpurun_out", "prof"),
+                    help="where --collect-counters keeps rocprofv3's raw output")
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"),
+                    help="where the counter summaries and records are written")
+    ap.add_argument("--counter-timeout", type=float, default=240.0, help="time limit of each rocprofv3 run (s)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -451,6 +483,11 @@ def main():
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
               "(each GPU would run the same kernel on its own heads); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.collect_counters:                 # child processes only; this one stays off the GPU
+        return collect_counters(args)
+    if args.summarize_counters:
+        return summarize_counters(args)
 
     import torch
     import io_aware_tiled_02_amd as fa
@@ -552,12 +589,266 @@ def main():
             "pct_of_peak": 100.0 * tflops / peak,
         },
         "roofline": roofline,
+        "counters": counters_for(cfg.index, ms),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (fp64 oracle on a sample of rows)")
         out["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+# ---- rocprofv3 counter collection (--collect-counters) ----
+# This mode never touches the GPU itself: every run is a child process,
+# rocprofv3 -- python3 bench.py ..., one counter pass per run (at most 8 SQ,
+# 2 GRBM and one of FETCH_SIZE / WRITE_SIZE each).
+XCDS, CUS, SIMDS_PER_CU = 8, 256, 4          # MI355X
+SQ_PASSES = [
+    ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES",
+     "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS"],
+    ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_VALU",
+     "SQ_ACTIVE_INST_LDS", "SQ_LDS_ADDR_CONFLICT", "SQ_WAIT_INST_ANY"],
+    ["GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_SALU", "SQ_ACTIVE_INST_ANY", "SQ_INSTS_VALU_TRANS_F32",
+     "SQ_LDS_DATA_FIFO_FULL", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_LDS_UNALIGNED_STALL"],
+]
+COPY_MIB = 512
+
+
+def _profile_tag(workload):
+    """(file-name tag, title) of a workload's profiles."""
+    if workload in ("fp8", "fp8-causal"):
+        c = gen.FP8[0 if workload == "fp8" else 1]
+        tag = f"fp8_d{c.d}_L{c.L}" + ("_causal" if c.causal else "")
+        return tag, f"FP8 scores, B={c.B} H={c.H} L={c.L} d={c.d}, {'causal' if c.causal else 'non-causal'}"
+    c = gen.config(int(workload))
+    tag = f"{gen.DTYPE_NAMES[c.dtype]}_d{c.d}_L{c.L}" + ("_causal" if c.causal else "")
+    return tag, (f"{gen.DTYPE_NAMES[c.dtype]}, B={c.B} H={c.H} L={c.L} d={c.d}, "
+                 f"{'causal' if c.causal else 'non-causal'}")
+
+
+def _rocprof(cmd_args, outdir, child, timeout_s):
+    """One rocprofv3 run of `child` (a bench.py command line); returns the command string."""
+    import subprocess
+    os.makedirs(outdir, exist_ok=True)
+    cmd = ["rocprofv3", *cmd_args, "-d", outdir, "-o", "fa", "--output-format", "csv", "--",
+           sys.executable, os.path.join(ROOT, "bench.py"), *child]
+    env = dict(os.environ, TMPDIR="/tmp")
+    shown = "cd /tmp && export TMPDIR=/tmp && " + " ".join(
+        c.replace(ROOT, "$GRAFT_REPO_ROOT").replace(sys.executable, "python3") for c in cmd)
+    print(f"[counters] {shown}", flush=True)
+    res = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True, timeout=timeout_s)
+    ok_line = any(l.startswith("{") for l in res.stdout.splitlines())
+    # rocprofv3 may end with SIGSEGV after the program finished and its files are whole
+    if res.returncode != 0 and not (res.returncode in (139, -11) and ok_line):
+        sys.stderr.write(res.stdout[-3000:] + res.stderr[-3000:])
+        raise SystemExit(f"rocprofv3 run failed with status {res.returncode}")
+    return shown
+
+
+def _csv_rows(outdir, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(outdir, "**", f"*{suffix}"), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {outdir}")
+    return rows
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row and row[n] != "":
+            return row[n]
+    raise KeyError(f"none of {names} in {sorted(row)}")
+
+
+def _counter_means(outdir, name_pred, last):
+    """Mean per dispatch over the last `last` dispatches of the kernels whose
+    name satisfies name_pred: ({counter: mean}, kernel name, dispatches)."""
+    per = {}
+    kname = None
+    for r in _csv_rows(outdir, "counter_collection.csv"):
+        name = _col(r, "Kernel_Name", "Kernel-Name", "KernelName")
+        if not name_pred(name):
+            continue
+        kname = name
+        did = int(_col(r, "Dispatch_Id", "Dispatch-Id", "Correlation_Id"))
+        cn = _col(r, "Counter_Name", "Counter-Name")
+        per.setdefault(did, {})
+        per[did][cn] = per[did].get(cn, 0.0) + float(_col(r, "Counter_Value", "Counter-Value"))
+    if not per:
+        raise SystemExit(f"no matching kernel in the counter files under {outdir}")
+    ids = sorted(per)[-last:]
+    names = set().union(*(per[i] for i in ids))
+    return {c: sum(per[i].get(c, 0.0) for i in ids) / len(ids) for c in names}, kname, len(ids)
+
+
+def _trace_durations_ns(outdir, name_pred, last):
+    rows = [r for r in _csv_rows(outdir, "kernel_trace.csv") if name_pred(_col(r, "Kernel_Name", "Kernel-Name"))]
+    rows.sort(key=lambda r: int(_col(r, "Start_Timestamp", "Start-Timestamp")))
+    d = [int(_col(r, "End_Timestamp", "End-Timestamp")) - int(_col(r, "Start_Timestamp", "Start-Timestamp"))
+         for r in rows]
+    return d[-last:], len(d)
+
+
+def _merge_record(path, sha, workload, entry, extra=None):
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    if rec.get("kernel_source_sha256") != sha:
+        rec = {"kernel_source_sha256": sha, "workloads": {}}     # records of another source are dropped
+    rec.update(extra or {})
+    rec.setdefault("workloads", {})[str(workload)] = entry
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+
+
+def collect_counters(args):
+    """Run the rocprofv3 passes on the workload's attention kernel (child
+    processes; raw output under --prof-dir, with a record of the commands),
+    then summarise them (summarize_counters)."""
+    wl = args.workload
+    if wl not in ("fp8", "fp8-causal") and not wl.isdigit():
+        raise SystemExit("--collect-counters takes a forward workload: 0..4, fp8 or fp8-causal")
+    tag, _ = _profile_tag(wl)
+    base = os.path.abspath(args.prof_dir)
+    T = args.counter_timeout
+    warm = args.warmup
+    child = ["--workload", wl, "--steps", "3", "--warmup", str(warm), "--no-cpu-baseline"]
+    cmds = {"kernel_source_sha256": kernel_digest(), "workload": wl, "steps": args.steps, "warmup": warm,
+            "pmc_steps": 3}
+    # 1. kernel trace with the bench's own step count
+    cmds["trace"] = _rocprof(["--kernel-trace", "--stats"], os.path.join(base, f"kt_{tag}"),
+                             ["--workload", wl, "--steps", str(args.steps), "--warmup", str(warm),
+                              "--no-cpu-baseline"], T)
+    # 2. SQ counter passes (the GRBM pass also records the kernel trace, for the clock)
+    cmds["sq"] = []
+    for i, counters in enumerate(SQ_PASSES):
+        extra = ["--kernel-trace"] if "GRBM_GUI_ACTIVE" in counters else []
+        cmds["sq"].append(_rocprof(["--pmc", *counters, *extra], os.path.join(base, f"sq{i}_{tag}"), child, T))
+    # 3. HBM traffic: FETCH_SIZE and WRITE_SIZE on the kernel and on a plain copy of known size
+    cmds["traffic"] = []
+    for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmds["traffic"].append(_rocprof(["--pmc", cn], os.path.join(base, f"{cn}_{tag}"), child, T))
+        cmds["traffic"].append(_rocprof(["--pmc", cn], os.path.join(base, f"{cn}_copy"),
+                                        ["--copy-probe", str(COPY_MIB)], T))
+    with open(os.path.join(base, f"commands_{tag}.json"), "w") as fh:
+        json.dump(cmds, fh, indent=1)
+    return summarize_counters(args)
+
+
+def summarize_counters(args):
+    """Derived figures from the raw rocprofv3 output of collect_counters (no GPU
+    needed): writes the kernel-trace, SQ-counter and traffic summaries and the
+    records the bench line reports, under --out-dir."""
+    wl = args.workload
+    tag, title = _profile_tag(wl)
+    base = os.path.abspath(args.prof_dir)
+    cmds = json.load(open(os.path.join(base, f"commands_{tag}.json")))
+    sha = cmds["kernel_source_sha256"]
+    if sha != kernel_digest():
+        raise SystemExit("the raw counters were taken on another kernel source than the one in this tree")
+    steps, warm, psteps = cmds["steps"], cmds["warmup"], cmds["pmc_steps"]
+    kshort = "fa_fwd_f32_kernel" if wl.isdigit() and gen.config(int(wl)).dtype == gen.F32 else "fa_fwd_h_kernel"
+    kpred = lambda n: kshort in n   # noqa: E731
+    pdir = os.path.abspath(args.out_dir)
+    os.makedirs(pdir, exist_ok=True)
+
+    kt = os.path.join(base, f"kt_{tag}")
+    st = [r for r in _csv_rows(kt, "kernel_stats.csv") if kpred(_col(r, "Name"))][0]
+    durs, ncalls = _trace_durations_ns(kt, kpred, steps)
+    kname = _col(st, "Name")
+    sq = {}
+    for i in range(len(SQ_PASSES)):
+        means, _, _ = _counter_means(os.path.join(base, f"sq{i}_{tag}"), kpred, psteps)
+        sq.update(means)
+    pmc_durs, _ = _trace_durations_ns(os.path.join(base, f"sq{len(SQ_PASSES) - 1}_{tag}"), kpred, psteps)
+    traffic = {}
+    copy_pred = lambda n: "copy" in n.lower() and "fill" not in n.lower()   # noqa: E731
+    for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+        kv, _, nk = _counter_means(os.path.join(base, f"{cn}_{tag}"), kpred, psteps)
+        cv, cname, ncp = _counter_means(os.path.join(base, f"{cn}_copy"), copy_pred, 3)
+        factor = (COPY_MIB << 20) / (cv[cn] * 1024.0)
+        traffic[cn] = {"kib": kv[cn], "n": nk, "copy_kib": cv[cn], "copy_n": ncp, "factor": factor,
+                       "bytes": kv[cn] * 1024.0 * factor, "copy_kernel": cname}
+
+    dur_ns = sum(pmc_durs) / len(pmc_durs)
+    cycles = sq["GRBM_GUI_ACTIVE"] / XCDS
+    simd_cycles = CUS * SIMDS_PER_CU * cycles
+    waves = sq["SQ_WAVES"]
+    hbm = traffic["FETCH_SIZE"]["bytes"] + traffic["WRITE_SIZE"]["bytes"]
+    c = gen.config(int(wl)) if wl.isdigit() else gen.FP8[0 if wl == "fp8" else 1]
+    algo, flops = c.algorithmic_bytes, c.flops
+    avg_ns = float(_col(st, "AverageNs", "Average_Ns"))
+    timed_ns = sum(durs) / len(durs)
+    derived = {
+        "kernel": kname,
+        "duration_ms_under_counters": dur_ns * 1e-6,
+        "engine_clock_ghz": cycles / dur_ns,
+        "mfma_busy": sq["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles,
+        "mfma_valu_coexec": sq["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cycles,
+        "lds_busy": sq["SQ_LDS_IDX_ACTIVE"] / (CUS * cycles),
+        "lds_bank_conflict_cycles": sq["SQ_LDS_BANK_CONFLICT"],
+        "per_wave": {k: sq[c_] / waves for k, c_ in (("valu", "SQ_INSTS_VALU"), ("mfma", "SQ_INSTS_MFMA"),
+                                                     ("lds", "SQ_INSTS_LDS"), ("salu", "SQ_INSTS_SALU"),
+                                                     ("v_exp_f32", "SQ_INSTS_VALU_TRANS_F32"))},
+        "trace_avg_ms": avg_ns * 1e-6,
+        "trace_timed_ms": timed_ns * 1e-6,
+        "summary": f"profiles/{kshort}_{tag}_sq_counters.md",
+    }
+    _merge_record(os.path.join(pdir, os.path.basename(COUNTER_FILE)), sha, wl, derived)
+    _merge_record(os.path.join(pdir, os.path.basename(TRAFFIC_FILE)), sha, wl, {
+        "kernel": kname,
+        "fetch_bytes_per_launch": traffic["FETCH_SIZE"]["bytes"],
+        "write_bytes_per_launch": traffic["WRITE_SIZE"]["bytes"],
+        "hbm_bytes_per_launch": hbm,
+        "algorithmic_bytes_per_launch": algo,
+    }, extra={"calibration": {"copy_bytes": COPY_MIB << 20, "fetch_factor": traffic["FETCH_SIZE"]["factor"],
+                              "write_factor": traffic["WRITE_SIZE"]["factor"]}})
+
+    head = (f"Kernel source sha256 (fa_fwd.hip then fa_device.h): `{sha}`\n\nKernel: `{kname}`\n\n"
+            "Written by `python bench.py --collect-counters --workload " + wl + "` from the raw rocprofv3 output of "
+            "the commands below (run from the repository root on the MI355X box).\n")
+    md = [f"# {kshort}, {title} — kernel trace\n", head, "```", cmds["trace"], "```\n",
+          "| calls | average (ns) | min (ns) | max (ns) | stddev (ns) |", "|---|---|---|---|---|",
+          f"| {_col(st, 'Calls')} | {avg_ns:.0f} | {_col(st, 'MinNs', 'Min_Ns')} | {_col(st, 'MaxNs', 'Max_Ns')} | "
+          f"{float(_col(st, 'StdDev', 'Stddev')):.0f} |\n",
+          f"Average over all {ncalls} calls, {warm} warm-up steps included: {avg_ns * 1e-6:.4f} ms, "
+          f"{flops / avg_ns * 1e-3:.1f} TFLOP/s. The last {len(durs)} calls (the bench's last timed loop"
+          + (", attention launches only" if not wl.isdigit() else "") + ") average "
+          f"{timed_ns * 1e-6:.4f} ms, {flops / timed_ns * 1e-3:.1f} TFLOP/s. The first warm-up calls run while the "
+          "engine clock ramps up."]
+    open(os.path.join(pdir, f"{kshort}_{tag}_kernel_trace.md"), "w").write("\n".join(md) + "\n")
+
+    md = [f"# {kshort}, {title} — SQ counters\n", head, "One counter pass per run:\n", "```", *cmds["sq"], "```\n",
+          f"| counter | mean per dispatch (last {psteps} dispatches) |", "|---|---|"]
+    md += [f"| {k} | {sq[k]:.6g} |" for k in sorted(sq)]
+    md += ["", f"Derived (GRBM_GUI_ACTIVE is summed over the {XCDS} XCDs; {CUS} CUs x {SIMDS_PER_CU} SIMDs; the "
+           "duration is the mean of the counted dispatches in the GRBM pass's kernel trace):", "",
+           f"- kernel duration under counters: {derived['duration_ms_under_counters']:.4f} ms; "
+           f"engine clock ≈ {derived['engine_clock_ghz']:.2f} GHz",
+           f"- MFMA busy: {derived['mfma_busy']:.3f} of SIMD cycles; MFMA and VALU co-issue: "
+           f"{derived['mfma_valu_coexec']:.3f}",
+           "- per wave: " + ", ".join(f"{k} {v:.0f}" for k, v in derived["per_wave"].items()),
+           f"- LDS bank-conflict cycles: {derived['lds_bank_conflict_cycles']:.0f}; "
+           f"LDS busy ≈ {derived['lds_busy']:.3f} of CU cycles"]
+    open(os.path.join(pdir, f"{kshort}_{tag}_sq_counters.md"), "w").write("\n".join(md) + "\n")
+
+    md = [f"# {kshort}, {title} — HBM traffic\n", head, "```", *cmds["traffic"], "```\n",
+          f"| counter | kernel (KiB/dispatch) | copy of {COPY_MIB} MiB (KiB/dispatch) | factor (true/counter) | "
+          "kernel bytes per launch |", "|---|---|---|---|---|"]
+    for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+        t = traffic[cn]
+        md.append(f"| {cn} | {t['kib']:.1f} (n={t['n']}) | {t['copy_kib']:.1f} (n={t['copy_n']}) | "
+                  f"{t['factor']:.4f} | {t['bytes']:,.0f} |")
+    md += ["", f"Copy kernel: `{traffic['FETCH_SIZE']['copy_kernel']}`. Kernel counts are the mean of the last "
+           f"{psteps} dispatches.", "",
+           f"HBM traffic per launch: {hbm:,.0f} B. Algorithmic bytes ("
+           + ("Q, K, V read once, O and lse written once" if wl.isdigit() else
+              "E4M3 codes of Q and K, their float32 block scales and V read once, O and lse written once")
+           + f"): {algo:,} B; ratio {hbm / algo:.4f}."]
+    open(os.path.join(pdir, f"{kshort}_{tag}_traffic.md"), "w").write("\n".join(md) + "\n")
+    print(json.dumps({"counters": derived, "hbm_bytes_per_launch": hbm, "algorithmic_bytes": algo}), flush=True)
 
 
 if __name__ == "__main__":

@@ -153,6 +153,16 @@ class Fp8Config:
         f = 4 * self.B * self.H * self.L * self.L * self.d
         return f // 2 if self.causal else f
 
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Bytes the attention kernel must move: the E4M3 codes of Q and K (one
+        byte each), V and O (two bytes each), lse, and the float32 block scales
+        of Q and K, each read or written once."""
+        n = self.B * self.H * self.L
+        nbq = -(-self.L // self.block_q)
+        nbk = -(-self.L // self.block_k)
+        return n * self.d * (1 + 1 + 2 + 2) + 4 * n + 4 * self.B * self.H * (nbq + nbk)
+
 
 # FP8 shapes: the peaked B1 H32 L8192 d128 workload (seed 3) and the causal
 # B2 H32 L4096 d128 one (seed 2), quantised in blocks of 128 rows.

@@ -150,3 +150,10 @@ def test_c_fill_range_and_error_codes():
     assert lib.fa_gen_fill(None, gen.F32, 0, 0, 0, 1.0) == 0
     assert lib.fa_gen_normal(None, 0, 1, 0, 0, 1.0) == -1
     np.testing.assert_array_equal(buf, 0)
+
+
+def test_fp8_algorithmic_bytes():
+    # B1 H32 L8192 d128, 128-row blocks: codes 2 x 32 MiB, V and O 2 x 64 MiB,
+    # lse 1 MiB, 2 x 32 x 64 float32 scales
+    c = gen.FP8[0]
+    assert c.algorithmic_bytes == 2 * 2**25 + 2 * 2**26 + 2**20 + 2 * 32 * 64 * 4 == 202391552
