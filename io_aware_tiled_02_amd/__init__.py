@@ -126,6 +126,17 @@ def fa_fwd_tiling(B, H, L, d, causal, dtype):
     return br.value, bc.value, wg.value
 
 
+def _check(t, name, shape, dtype, device):
+    """A caller-given tensor must be a contiguous device tensor of exactly this
+    shape and dtype on `device`: the kernels index it as such, so anything
+    else would be read or written out of bounds."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}"
+                         + ("" if t.is_contiguous() else " (not contiguous)"))
+
+
 def _dtype_code(t) -> int:
     import torch
     codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
@@ -146,13 +157,15 @@ def forward(q, k, v, scale: float, causal: bool = False, out=None, lse=None, str
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
     for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous tensors on one device")
     B, H, L, d = q.shape
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    _check(out, "out", q.shape, q.dtype, q.device)
+    _check(lse, "lse", (B, H, L), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -177,15 +190,19 @@ def forward_splitkv(q, k, v, scale: float, nsplit: int = 0, out=None, lse=None, 
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
     for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous tensors on one device")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    _check(out, "out", q.shape, q.dtype, q.device)
+    _check(lse, "lse", (B, H, Lq), torch.float32, q.device)
     need = fa_splitkv_workspace_bytes(B, H, Lq, Lk, d, nsplit)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -199,14 +216,18 @@ def forward_splitkv(q, k, v, scale: float, nsplit: int = 0, out=None, lse=None, 
 def backward(q, k, v, o, lse, dout, scale: float, causal: bool = False, workspace=None, stream=None):
     """dq, dk, dv for torch device tensors (B, H, L, d); o, lse from forward()."""
     import torch
-    for t in (q, k, v, o, dout):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v, o, dout must be contiguous device tensors of one shape and dtype")
+    if q.dim() != 4:
+        raise ValueError("q must be (B, H, L, d)")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check(t, name, q.shape, q.dtype, q.device)
     B, H, L, d = q.shape
+    _check(lse, "lse", (B, H, L), torch.float32, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     need = fa_bwd_workspace_bytes(B, H, L)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
@@ -225,10 +246,14 @@ def quantize_fp8(x, block: int, x8=None, scales=None, stream=None):
     if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous (B, H, L, d) device tensor")
     B, H, L, d = x.shape
+    if block < 1:
+        raise ValueError("block must be >= 1")
     if x8 is None:
         x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((B * H, (L + block - 1) // block), dtype=torch.float32, device=x.device)
+    _check(x8, "x8", x.shape, torch.uint8, x.device)
+    _check(scales, "scales", (B * H, (L + block - 1) // block), torch.float32, x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     rc = fa_quantize_fp8(x.data_ptr(), _dtype_code(x), B, H, L, d, int(block), x8.data_ptr(), scales.data_ptr(),
@@ -248,16 +273,21 @@ def forward_fp8(q8, k8, q_scale, k_scale, v, scale: float, causal: bool, block_q
     if q8.dtype != torch.uint8 or k8.dtype != torch.uint8:
         raise TypeError("q8 and k8 hold E4M3 codes as uint8")
     for t in (q8, k8, q_scale, k_scale, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("inputs must be contiguous device tensors")
+        if not t.is_cuda or not t.is_contiguous() or t.device != v.device:
+            raise ValueError("inputs must be contiguous tensors on one device")
     B, H, L, d = q8.shape
-    if q_scale.numel() != B * H * ((L + block_q - 1) // block_q) or \
+    if block_q < 1 or block_k < 1:
+        raise ValueError("block_q and block_k must be >= 1")
+    if q_scale.dtype != torch.float32 or k_scale.dtype != torch.float32 or \
+            q_scale.numel() != B * H * ((L + block_q - 1) // block_q) or \
             k_scale.numel() != B * H * ((L + block_k - 1) // block_k):
         raise ValueError("scale tensors must hold B*H*ceil(L/block) float32 values")
     if out is None:
         out = torch.empty_like(v)
     if lse is None:
         lse = torch.empty((B, H, L), dtype=torch.float32, device=v.device)
+    _check(out, "out", v.shape, v.dtype, v.device)
+    _check(lse, "lse", (B, H, L), torch.float32, v.device)
     if stream is None:
         stream = torch.cuda.current_stream(v.device)
     rc = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(), v.data_ptr(),
