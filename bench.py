@@ -27,51 +27,71 @@ import fa_inputs as gen  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s (4·B·H·L²·d) and % of MI355X bf16 MFMA peak"
 PEAK_TFLOPS = {gen.BF16: 2516.6, gen.F16: 2516.6, gen.F32: 157.3}   # dense MFMA peaks, MI355X
-# the sources the forward kernel is compiled from (the traffic record is keyed to them)
-KERNEL_SRCS = [os.path.join(ROOT, "io_aware_tiled_02_amd", "csrc", n) for n in ("fa_fwd.hip", "fa_device.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_kernel.json")
-COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_fa_fwd_kernel.json")
+CSRC = os.path.join(ROOT, "io_aware_tiled_02_amd", "csrc")
+# kernel families: the sources their kernels are compiled from (the counter
+# and traffic records of a family are keyed to these files' sha256) and the
+# name of their record files under profiles/
+FAMILIES = {
+    "fwd": {"srcs": ("fa_fwd.hip", "fa_device.h"), "record": "fa_fwd_kernel"},
+    "splitkv": {"srcs": ("fa_splitkv.hip", "fa_device.h"), "record": "fa_splitkv_kernels"},
+    "bwd": {"srcs": ("fa_bwd.hip", "fa_device.h"), "record": "fa_bwd_kernels"},
+}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_digest() -> str:
+def _family(workload) -> str:
+    w = str(workload)
+    return "splitkv" if w == "decode" else "bwd" if w.startswith("bwd") else "fwd"
+
+
+def kernel_digest(family: str = "fwd") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SRCS:
-        h.update(open(p, "rb").read())
+    for n in FAMILIES[family]["srcs"]:
+        h.update(open(os.path.join(CSRC, n), "rb").read())
     return h.hexdigest()
 
 
+def _record_path(kind, family):
+    return os.path.join(ROOT, "profiles", f"{kind}_{FAMILIES[family]['record']}.json")
+
+
+def _record(kind, workload):
+    """The workload's entry of a counter or traffic record, if the record was
+    taken on the kernel sources of this tree."""
+    fam = _family(workload)
+    path = _record_path(kind, fam)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256") != kernel_digest(fam):
+        return None
+    return rec.get("workloads", {}).get(str(workload))
+
+
 def traffic_for(workload):
-    """Measured HBM bytes per launch of the workload's attention kernel (key: the
-    workload index, or 'fp8'), if the counters were taken on this exact kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    rec = json.load(open(TRAFFIC_FILE))
-    if rec.get("kernel_source_sha256") != kernel_digest():
-        return None
-    w = rec.get("workloads", {}).get(str(workload))
-    if not w:
-        return None
-    return w["hbm_bytes_per_launch"]
+    """Measured HBM bytes of one call (all of its kernels) for a workload
+    (0..4, fp8, fp8-causal, decode, bwd, bwd-causal), if the counters were taken
+    on the current kernel sources."""
+    w = _record("traffic", workload)
+    return w["hbm_bytes_per_launch"] if w else None
 
 
 def counters_for(workload, ms_per_launch):
-    """SQ-counter figures of the workload's attention kernel (rocprofv3 --pmc runs
-    made by --collect-counters), if they were taken on this exact kernel source;
-    with the achieved HBM rate of this run when the traffic record exists."""
-    if not os.path.exists(COUNTER_FILE):
-        return None
-    rec = json.load(open(COUNTER_FILE))
-    if rec.get("kernel_source_sha256") != kernel_digest():
-        return None
-    w = rec.get("workloads", {}).get(str(workload))
+    """SQ-counter figures of the workload's kernels (rocprofv3 --pmc runs made by
+    --collect-counters), if they were taken on the current kernel sources; with
+    the achieved HBM rate of this run when the traffic record exists."""
+    w = _record("counters", workload)
     if not w:
         return None
-    out = {k: w[k] for k in ("mfma_busy", "mfma_valu_coexec", "lds_busy", "lds_bank_conflict_cycles",
-                             "engine_clock_ghz", "duration_ms_under_counters", "summary") if k in w}
+    keys = ("mfma_busy", "mfma_valu_coexec", "lds_busy", "lds_bank_conflict_cycles", "engine_clock_ghz",
+            "duration_ms_under_counters", "hbm_gbps_under_counters")
+    out = {k: w[k] for k in keys if k in w}
+    if "kernels" in w:
+        out["kernels"] = {n: {k: v[k] for k in keys if k in v} for n, v in w["kernels"].items()}
+    out["summary"] = w.get("summary")
     traffic = traffic_for(workload)
     if traffic is not None and ms_per_launch:
         out["hbm_gbps"] = traffic / (ms_per_launch * 1e-3) / 1e9
@@ -204,11 +224,12 @@ def bench_decode(args, torch, fa):
             "peak": 8000.0,
             "unit": "GB/s",
             "frac": gbs / 8000.0,
-            "traffic": None,
+            "traffic": traffic_for("decode"),
             "kernel": "fa_splitkv_kernel + fa_combine_kernel (one fa_fwd_splitkv call)",
             "algorithmic_bytes_per_launch": cfg.algorithmic_bytes,
             "avg_launch_ms": ms,
         },
+        "counters": counters_for("decode", ms),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -308,11 +329,13 @@ def bench_bwd(args, torch, fa, cfg):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": tflops / peak,
-            "traffic": None,
+            "traffic": traffic_for(args.workload),
             "kernel": "fa_bwd_pre_kernel + fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (one fa_bwd call)",
             "per_launch_flops": cfg.flops,
             "avg_launch_ms": ms,
+            "algorithmic_bytes_per_launch": cfg.algorithmic_bytes,
         },
+        "counters": counters_for(args.workload, ms),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -614,16 +637,44 @@ SQ_PASSES = [
 COPY_MIB = 512
 
 
-def _profile_tag(workload):
-    """(file-name tag, title) of a workload's profiles."""
-    if workload in ("fp8", "fp8-causal"):
-        c = gen.FP8[0 if workload == "fp8" else 1]
-        tag = f"fp8_d{c.d}_L{c.L}" + ("_causal" if c.causal else "")
-        return tag, f"FP8 scores, B={c.B} H={c.H} L={c.L} d={c.d}, {'causal' if c.causal else 'non-causal'}"
-    c = gen.config(int(workload))
-    tag = f"{gen.DTYPE_NAMES[c.dtype]}_d{c.d}_L{c.L}" + ("_causal" if c.causal else "")
-    return tag, (f"{gen.DTYPE_NAMES[c.dtype]}, B={c.B} H={c.H} L={c.L} d={c.d}, "
-                 f"{'causal' if c.causal else 'non-causal'}")
+def _workload_spec(wl):
+    """What --collect-counters profiles for a bench workload: its kernel family,
+    file tag and title, the kernels of one call (name substrings), their FLOPs
+    per launch, and the algorithmic bytes of one call."""
+    def causal_s(c):
+        return "causal" if c.causal else "non-causal"
+    if wl.isdigit():
+        c = gen.config(int(wl))
+        k = "fa_fwd_f32_kernel" if c.dtype == gen.F32 else "fa_fwd_h_kernel"
+        return dict(family="fwd", prefix=k, kernels=[k], flops={k: c.flops}, algo=c.algorithmic_bytes,
+                    tag=f"{gen.DTYPE_NAMES[c.dtype]}_d{c.d}_L{c.L}" + ("_causal" if c.causal else ""),
+                    title=f"{gen.DTYPE_NAMES[c.dtype]}, B={c.B} H={c.H} L={c.L} d={c.d}, {causal_s(c)}",
+                    algo_what="Q, K, V read once, O and lse written once")
+    if wl in ("fp8", "fp8-causal"):
+        c = gen.FP8[0 if wl == "fp8" else 1]
+        k = "fa_fwd_h_kernel"
+        return dict(family="fwd", prefix=k, kernels=[k], flops={k: c.flops}, algo=c.algorithmic_bytes,
+                    tag=f"fp8_d{c.d}_L{c.L}" + ("_causal" if c.causal else ""),
+                    title=f"FP8 scores, B={c.B} H={c.H} L={c.L} d={c.d}, {causal_s(c)}",
+                    algo_what="E4M3 codes of Q and K, their float32 block scales and V read once, O and lse "
+                              "written once")
+    if wl == "decode":
+        c = gen.DECODE
+        ks = ["fa_splitkv_kernel", "fa_combine_kernel"]
+        return dict(family="splitkv", prefix="fa_splitkv_kernels", kernels=ks, flops={}, algo=c.algorithmic_bytes,
+                    tag=f"{gen.DTYPE_NAMES[c.dtype]}_d{c.d}_decode_Lk{c.Lk}",
+                    title=f"{gen.DTYPE_NAMES[c.dtype]} decode, B={c.B} H={c.H} Lq={c.Lq} Lk={c.Lk} d={c.d}",
+                    algo_what="Q, K, V read once, O and lse written once")
+    if wl in ("bwd", "bwd-causal"):
+        c = gen.BWD[0 if wl == "bwd" else 1]
+        ks = ["fa_bwd_dkdv_kernel", "fa_bwd_dq_kernel", "fa_bwd_pre_kernel"]
+        # dK/dV forms S, dP, dV, dK (4 of the 5 products); dQ forms S, dP, dQ
+        return dict(family="bwd", prefix="fa_bwd_kernels", kernels=ks,
+                    flops={ks[0]: c.flops * 4 // 5, ks[1]: c.flops * 3 // 5, ks[2]: 0}, algo=c.algorithmic_bytes,
+                    tag=f"{gen.DTYPE_NAMES[c.dtype]}_d{c.d}_L{c.L}" + ("_causal" if c.causal else ""),
+                    title=f"backward, {gen.DTYPE_NAMES[c.dtype]}, B={c.B} H={c.H} L={c.L} d={c.d}, {causal_s(c)}",
+                    algo_what="Q, K, V, O, dO and lse read once, dQ, dK, dV written once")
+    raise SystemExit("--collect-counters takes a bench workload: 0..4, fp8, fp8-causal, decode, bwd, bwd-causal")
 
 
 def _rocprof(cmd_args, outdir, child, timeout_s):
@@ -704,35 +755,35 @@ def _merge_record(path, sha, workload, entry, extra=None):
 
 
 def collect_counters(args):
-    """Run the rocprofv3 passes on the workload's attention kernel (child
-    processes; raw output under --prof-dir, with a record of the commands),
-    then summarise them (summarize_counters)."""
+    """Run the rocprofv3 passes on the workload's kernels (child processes; raw
+    output under --prof-dir, with a record of the commands), then summarise them
+    (summarize_counters)."""
     wl = args.workload
-    if wl not in ("fp8", "fp8-causal") and not wl.isdigit():
-        raise SystemExit("--collect-counters takes a forward workload: 0..4, fp8 or fp8-causal")
-    tag, _ = _profile_tag(wl)
+    spec = _workload_spec(wl)
+    tag = spec["tag"]
+    raw = f"{spec['prefix']}_{tag}"               # raw output directories of this workload
     base = os.path.abspath(args.prof_dir)
     T = args.counter_timeout
     warm = args.warmup
     child = ["--workload", wl, "--steps", "3", "--warmup", str(warm), "--no-cpu-baseline"]
-    cmds = {"kernel_source_sha256": kernel_digest(), "workload": wl, "steps": args.steps, "warmup": warm,
-            "pmc_steps": 3}
+    cmds = {"kernel_source_sha256": kernel_digest(spec["family"]), "workload": wl, "steps": args.steps,
+            "warmup": warm, "pmc_steps": 3}
     # 1. kernel trace with the bench's own step count
-    cmds["trace"] = _rocprof(["--kernel-trace", "--stats"], os.path.join(base, f"kt_{tag}"),
+    cmds["trace"] = _rocprof(["--kernel-trace", "--stats"], os.path.join(base, f"kt_{raw}"),
                              ["--workload", wl, "--steps", str(args.steps), "--warmup", str(warm),
                               "--no-cpu-baseline"], T)
     # 2. SQ counter passes (the GRBM pass also records the kernel trace, for the clock)
     cmds["sq"] = []
     for i, counters in enumerate(SQ_PASSES):
         extra = ["--kernel-trace"] if "GRBM_GUI_ACTIVE" in counters else []
-        cmds["sq"].append(_rocprof(["--pmc", *counters, *extra], os.path.join(base, f"sq{i}_{tag}"), child, T))
-    # 3. HBM traffic: FETCH_SIZE and WRITE_SIZE on the kernel and on a plain copy of known size
+        cmds["sq"].append(_rocprof(["--pmc", *counters, *extra], os.path.join(base, f"sq{i}_{raw}"), child, T))
+    # 3. HBM traffic: FETCH_SIZE and WRITE_SIZE on the kernels and on a plain copy of known size
     cmds["traffic"] = []
     for cn in ("FETCH_SIZE", "WRITE_SIZE"):
-        cmds["traffic"].append(_rocprof(["--pmc", cn], os.path.join(base, f"{cn}_{tag}"), child, T))
+        cmds["traffic"].append(_rocprof(["--pmc", cn], os.path.join(base, f"{cn}_{raw}"), child, T))
         cmds["traffic"].append(_rocprof(["--pmc", cn], os.path.join(base, f"{cn}_copy"),
                                         ["--copy-probe", str(COPY_MIB)], T))
-    with open(os.path.join(base, f"commands_{tag}.json"), "w") as fh:
+    with open(os.path.join(base, f"commands_{raw}.json"), "w") as fh:
         json.dump(cmds, fh, indent=1)
     return summarize_counters(args)
 
@@ -742,113 +793,143 @@ def summarize_counters(args):
     needed): writes the kernel-trace, SQ-counter and traffic summaries and the
     records the bench line reports, under --out-dir."""
     wl = args.workload
-    tag, title = _profile_tag(wl)
+    spec = _workload_spec(wl)
+    tag, title, fam = spec["tag"], spec["title"], spec["family"]
+    raw = f"{spec['prefix']}_{tag}"
     base = os.path.abspath(args.prof_dir)
-    cmds = json.load(open(os.path.join(base, f"commands_{tag}.json")))
+    cmds = json.load(open(os.path.join(base, f"commands_{raw}.json")))
     sha = cmds["kernel_source_sha256"]
-    if sha != kernel_digest():
+    if sha != kernel_digest(fam):
         raise SystemExit("the raw counters were taken on another kernel source than the one in this tree")
     steps, warm, psteps = cmds["steps"], cmds["warmup"], cmds["pmc_steps"]
-    kshort = "fa_fwd_f32_kernel" if wl.isdigit() and gen.config(int(wl)).dtype == gen.F32 else "fa_fwd_h_kernel"
-    kpred = lambda n: kshort in n   # noqa: E731
     pdir = os.path.abspath(args.out_dir)
     os.makedirs(pdir, exist_ok=True)
+    preds = {k: (lambda n, k=k: k in n) for k in spec["kernels"]}
+    srcs = " then ".join(FAMILIES[fam]["srcs"])
 
-    kt = os.path.join(base, f"kt_{tag}")
-    st = [r for r in _csv_rows(kt, "kernel_stats.csv") if kpred(_col(r, "Name"))][0]
-    durs, ncalls = _trace_durations_ns(kt, kpred, steps)
-    kname = _col(st, "Name")
-    sq = {}
-    for i in range(len(SQ_PASSES)):
-        means, _, _ = _counter_means(os.path.join(base, f"sq{i}_{tag}"), kpred, psteps)
-        sq.update(means)
-    pmc_durs, _ = _trace_durations_ns(os.path.join(base, f"sq{len(SQ_PASSES) - 1}_{tag}"), kpred, psteps)
-    traffic = {}
+    kt = os.path.join(base, f"kt_{raw}")
+    stats_rows = _csv_rows(kt, "kernel_stats.csv")
+    per = {}
+    for k in spec["kernels"]:
+        st = [r for r in stats_rows if preds[k](_col(r, "Name"))][0]
+        durs, ncalls = _trace_durations_ns(kt, preds[k], steps)
+        sq = {}
+        for i in range(len(SQ_PASSES)):
+            sq.update(_counter_means(os.path.join(base, f"sq{i}_{raw}"), preds[k], psteps)[0])
+        pmc_durs, _ = _trace_durations_ns(os.path.join(base, f"sq{len(SQ_PASSES) - 1}_{raw}"), preds[k], psteps)
+        per[k] = dict(name=_col(st, "Name"), st=st, durs=durs, ncalls=ncalls, sq=sq, pmc_durs=pmc_durs)
+    traffic, calib = {}, {}
     copy_pred = lambda n: "copy" in n.lower() and "fill" not in n.lower()   # noqa: E731
     for cn in ("FETCH_SIZE", "WRITE_SIZE"):
-        kv, _, nk = _counter_means(os.path.join(base, f"{cn}_{tag}"), kpred, psteps)
         cv, cname, ncp = _counter_means(os.path.join(base, f"{cn}_copy"), copy_pred, 3)
         factor = (COPY_MIB << 20) / (cv[cn] * 1024.0)
-        traffic[cn] = {"kib": kv[cn], "n": nk, "copy_kib": cv[cn], "copy_n": ncp, "factor": factor,
-                       "bytes": kv[cn] * 1024.0 * factor, "copy_kernel": cname}
+        calib[cn] = dict(copy_kib=cv[cn], copy_n=ncp, factor=factor, copy_kernel=cname)
+        for k in spec["kernels"]:
+            kv, _, nk = _counter_means(os.path.join(base, f"{cn}_{raw}"), preds[k], psteps)
+            traffic.setdefault(k, {})[cn] = dict(kib=kv[cn], n=nk, bytes=kv[cn] * 1024.0 * factor)
 
-    dur_ns = sum(pmc_durs) / len(pmc_durs)
-    cycles = sq["GRBM_GUI_ACTIVE"] / XCDS
-    simd_cycles = CUS * SIMDS_PER_CU * cycles
-    waves = sq["SQ_WAVES"]
-    hbm = traffic["FETCH_SIZE"]["bytes"] + traffic["WRITE_SIZE"]["bytes"]
-    c = gen.config(int(wl)) if wl.isdigit() else gen.FP8[0 if wl == "fp8" else 1]
-    algo, flops = c.algorithmic_bytes, c.flops
-    avg_ns = float(_col(st, "AverageNs", "Average_Ns"))
-    timed_ns = sum(durs) / len(durs)
-    derived = {
-        "kernel": kname,
-        "duration_ms_under_counters": dur_ns * 1e-6,
-        "engine_clock_ghz": cycles / dur_ns,
-        "mfma_busy": sq["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles,
-        "mfma_valu_coexec": sq["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cycles,
-        "lds_busy": sq["SQ_LDS_IDX_ACTIVE"] / (CUS * cycles),
-        "lds_bank_conflict_cycles": sq["SQ_LDS_BANK_CONFLICT"],
-        "per_wave": {k: sq[c_] / waves for k, c_ in (("valu", "SQ_INSTS_VALU"), ("mfma", "SQ_INSTS_MFMA"),
-                                                     ("lds", "SQ_INSTS_LDS"), ("salu", "SQ_INSTS_SALU"),
-                                                     ("v_exp_f32", "SQ_INSTS_VALU_TRANS_F32"))},
-        "trace_avg_ms": avg_ns * 1e-6,
-        "trace_timed_ms": timed_ns * 1e-6,
-        "summary": f"profiles/{kshort}_{tag}_sq_counters.md",
-    }
-    _merge_record(os.path.join(pdir, os.path.basename(COUNTER_FILE)), sha, wl, derived)
-    _merge_record(os.path.join(pdir, os.path.basename(TRAFFIC_FILE)), sha, wl, {
-        "kernel": kname,
-        "fetch_bytes_per_launch": traffic["FETCH_SIZE"]["bytes"],
-        "write_bytes_per_launch": traffic["WRITE_SIZE"]["bytes"],
-        "hbm_bytes_per_launch": hbm,
-        "algorithmic_bytes_per_launch": algo,
-    }, extra={"calibration": {"copy_bytes": COPY_MIB << 20, "fetch_factor": traffic["FETCH_SIZE"]["factor"],
-                              "write_factor": traffic["WRITE_SIZE"]["factor"]}})
+    derived = {}
+    for k in spec["kernels"]:
+        q = per[k]
+        sq = q["sq"]
+        dur_ns = sum(q["pmc_durs"]) / len(q["pmc_durs"])
+        cycles = sq["GRBM_GUI_ACTIVE"] / XCDS
+        simd_cycles = CUS * SIMDS_PER_CU * cycles
+        hbm_k = traffic[k]["FETCH_SIZE"]["bytes"] + traffic[k]["WRITE_SIZE"]["bytes"]
+        derived[k] = {
+            "kernel": q["name"],
+            "duration_ms_under_counters": dur_ns * 1e-6,
+            # GRBM_GUI_ACTIVE also counts the GPU's activity around a dispatch:
+            # no clock figure for dispatches too short for that to vanish
+            "engine_clock_ghz": cycles / dur_ns if dur_ns >= 1e5 else None,
+            "mfma_busy": sq["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles,
+            "mfma_valu_coexec": sq["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cycles,
+            "lds_busy": sq["SQ_LDS_IDX_ACTIVE"] / (CUS * cycles),
+            "lds_bank_conflict_cycles": sq["SQ_LDS_BANK_CONFLICT"],
+            "hbm_gbps_under_counters": hbm_k / dur_ns,
+            "per_wave": {n: sq[c_] / sq["SQ_WAVES"] for n, c_ in (
+                ("valu", "SQ_INSTS_VALU"), ("mfma", "SQ_INSTS_MFMA"), ("lds", "SQ_INSTS_LDS"),
+                ("salu", "SQ_INSTS_SALU"), ("v_exp_f32", "SQ_INSTS_VALU_TRANS_F32"))},
+            "trace_avg_ms": float(_col(q["st"], "AverageNs", "Average_Ns")) * 1e-6,
+            "trace_timed_ms": sum(q["durs"]) / len(q["durs"]) * 1e-6,
+            "hbm_bytes_per_launch": hbm_k,
+        }
+    hbm = sum(derived[k]["hbm_bytes_per_launch"] for k in spec["kernels"])
+    prefix = spec["prefix"]
+    summary = f"profiles/{prefix}_{tag}_sq_counters.md"
+    if len(spec["kernels"]) == 1:
+        entry = dict(derived[spec["kernels"][0]], summary=summary)
+        tentry = {"kernel": per[spec["kernels"][0]]["name"],
+                  "fetch_bytes_per_launch": traffic[spec["kernels"][0]]["FETCH_SIZE"]["bytes"],
+                  "write_bytes_per_launch": traffic[spec["kernels"][0]]["WRITE_SIZE"]["bytes"]}
+    else:
+        entry = {"kernels": derived, "summary": summary}
+        tentry = {"kernels": {k: {"fetch_bytes_per_launch": traffic[k]["FETCH_SIZE"]["bytes"],
+                                  "write_bytes_per_launch": traffic[k]["WRITE_SIZE"]["bytes"]}
+                              for k in spec["kernels"]}}
+    tentry.update(hbm_bytes_per_launch=hbm, algorithmic_bytes_per_launch=spec["algo"])
+    _merge_record(os.path.join(pdir, os.path.basename(_record_path("counters", fam))), sha, wl, entry)
+    _merge_record(os.path.join(pdir, os.path.basename(_record_path("traffic", fam))), sha, wl, tentry,
+                  extra={"calibration": {"copy_bytes": COPY_MIB << 20, "fetch_factor": calib["FETCH_SIZE"]["factor"],
+                                         "write_factor": calib["WRITE_SIZE"]["factor"]}})
 
-    head = (f"Kernel source sha256 (fa_fwd.hip then fa_device.h): `{sha}`\n\nKernel: `{kname}`\n\n"
-            "Written by `python bench.py --collect-counters --workload " + wl + "` from the raw rocprofv3 output of "
-            "the commands below (run from the repository root on the MI355X box).\n")
-    md = [f"# {kshort}, {title} — kernel trace\n", head, "```", cmds["trace"], "```\n",
-          "| calls | average (ns) | min (ns) | max (ns) | stddev (ns) |", "|---|---|---|---|---|",
-          f"| {_col(st, 'Calls')} | {avg_ns:.0f} | {_col(st, 'MinNs', 'Min_Ns')} | {_col(st, 'MaxNs', 'Max_Ns')} | "
-          f"{float(_col(st, 'StdDev', 'Stddev')):.0f} |\n",
-          f"Average over all {ncalls} calls, {warm} warm-up steps included: {avg_ns * 1e-6:.4f} ms, "
-          f"{flops / avg_ns * 1e-3:.1f} TFLOP/s. The last {len(durs)} calls (the bench's last timed loop"
-          + (", attention launches only" if not wl.isdigit() else "") + ") average "
-          f"{timed_ns * 1e-6:.4f} ms, {flops / timed_ns * 1e-3:.1f} TFLOP/s. The first warm-up calls run while the "
-          "engine clock ramps up."]
-    open(os.path.join(pdir, f"{kshort}_{tag}_kernel_trace.md"), "w").write("\n".join(md) + "\n")
+    head = (f"Kernel source sha256 ({srcs}): `{sha}`\n\n"
+            + "".join(f"Kernel: `{per[k]['name']}`\n\n" for k in spec["kernels"])
+            + "Written by `python bench.py --collect-counters --workload " + wl + "` from the raw rocprofv3 output "
+            "of the commands below (run from the repository root on the MI355X box).\n")
+    md = [f"# {prefix}, {title} — kernel trace\n", head, "```", cmds["trace"], "```\n",
+          "| kernel | calls | average (ns) | min (ns) | max (ns) | stddev (ns) | last timed calls (ns) | TFLOP/s there |",
+          "|---|---|---|---|---|---|---|---|"]
+    for k in spec["kernels"]:
+        q, st = per[k], per[k]["st"]
+        tms = sum(q["durs"]) / len(q["durs"])
+        fl = spec["flops"].get(k)
+        md.append(f"| `{k}` | {_col(st, 'Calls')} | {float(_col(st, 'AverageNs', 'Average_Ns')):.0f} | "
+                  f"{_col(st, 'MinNs', 'Min_Ns')} | {_col(st, 'MaxNs', 'Max_Ns')} | "
+                  f"{float(_col(st, 'StdDev', 'Stddev')):.0f} | {tms:.0f} (last {len(q['durs'])}) | "
+                  + (f"{fl / tms * 1e-3:.1f}" if fl else "—") + " |")
+    md += ["", f"Each kernel's calls include the {warm} warm-up steps; the last-calls column covers the bench's "
+           "last timed loop" + (" (attention launches only)" if wl.startswith("fp8") else "")
+           + ". The first warm-up calls run while the engine clock ramps up."]
+    open(os.path.join(pdir, f"{prefix}_{tag}_kernel_trace.md"), "w").write("\n".join(md) + "\n")
 
-    md = [f"# {kshort}, {title} — SQ counters\n", head, "One counter pass per run:\n", "```", *cmds["sq"], "```\n",
-          f"| counter | mean per dispatch (last {psteps} dispatches) |", "|---|---|"]
-    md += [f"| {k} | {sq[k]:.6g} |" for k in sorted(sq)]
-    md += ["", f"Derived (GRBM_GUI_ACTIVE is summed over the {XCDS} XCDs; {CUS} CUs x {SIMDS_PER_CU} SIMDs; the "
-           "duration is the mean of the counted dispatches in the GRBM pass's kernel trace):", "",
-           f"- kernel duration under counters: {derived['duration_ms_under_counters']:.4f} ms; "
-           f"engine clock ≈ {derived['engine_clock_ghz']:.2f} GHz",
-           f"- MFMA busy: {derived['mfma_busy']:.3f} of SIMD cycles; MFMA and VALU co-issue: "
-           f"{derived['mfma_valu_coexec']:.3f}",
-           "- per wave: " + ", ".join(f"{k} {v:.0f}" for k, v in derived["per_wave"].items()),
-           f"- LDS bank-conflict cycles: {derived['lds_bank_conflict_cycles']:.0f}; "
-           f"LDS busy ≈ {derived['lds_busy']:.3f} of CU cycles"]
-    open(os.path.join(pdir, f"{kshort}_{tag}_sq_counters.md"), "w").write("\n".join(md) + "\n")
+    names = sorted(set().union(*(per[k]["sq"] for k in spec["kernels"])))
+    md = [f"# {prefix}, {title} — SQ counters\n", head, "One counter pass per run:\n", "```", *cmds["sq"], "```\n",
+          f"Mean per dispatch over each kernel's last {psteps} dispatches:\n",
+          "| counter | " + " | ".join(f"`{k}`" for k in spec["kernels"]) + " |",
+          "|---|" + "---|" * len(spec["kernels"])]
+    md += [f"| {n} | " + " | ".join(f"{per[k]['sq'].get(n, float('nan')):.6g}" for k in spec["kernels"]) + " |"
+           for n in names]
+    md += ["", f"Derived (GRBM_GUI_ACTIVE is summed over the {XCDS} XCDs; {CUS} CUs x {SIMDS_PER_CU} SIMDs; each "
+           "duration is the mean of the counted dispatches in the GRBM pass's kernel trace):", ""]
+    for k in spec["kernels"]:
+        d_ = derived[k]
+        clk = (f"engine clock ≈ {d_['engine_clock_ghz']:.2f} GHz" if d_["engine_clock_ghz"] is not None
+               else "too short for a clock figure")
+        md += [f"- `{k}`: duration under counters {d_['duration_ms_under_counters']:.4f} ms; {clk}; "
+               f"MFMA busy {d_['mfma_busy']:.3f} of SIMD cycles, MFMA and VALU "
+               f"co-issue {d_['mfma_valu_coexec']:.3f}; LDS busy ≈ {d_['lds_busy']:.3f} of CU cycles, bank-conflict "
+               f"cycles {d_['lds_bank_conflict_cycles']:.0f}; HBM {d_['hbm_gbps_under_counters']:.0f} GB/s; per wave: "
+               + ", ".join(f"{n} {v:.0f}" for n, v in d_["per_wave"].items())]
+    open(os.path.join(pdir, f"{prefix}_{tag}_sq_counters.md"), "w").write("\n".join(md) + "\n")
 
-    md = [f"# {kshort}, {title} — HBM traffic\n", head, "```", *cmds["traffic"], "```\n",
-          f"| counter | kernel (KiB/dispatch) | copy of {COPY_MIB} MiB (KiB/dispatch) | factor (true/counter) | "
-          "kernel bytes per launch |", "|---|---|---|---|---|"]
-    for cn in ("FETCH_SIZE", "WRITE_SIZE"):
-        t = traffic[cn]
-        md.append(f"| {cn} | {t['kib']:.1f} (n={t['n']}) | {t['copy_kib']:.1f} (n={t['copy_n']}) | "
-                  f"{t['factor']:.4f} | {t['bytes']:,.0f} |")
-    md += ["", f"Copy kernel: `{traffic['FETCH_SIZE']['copy_kernel']}`. Kernel counts are the mean of the last "
-           f"{psteps} dispatches.", "",
-           f"HBM traffic per launch: {hbm:,.0f} B. Algorithmic bytes ("
-           + ("Q, K, V read once, O and lse written once" if wl.isdigit() else
-              "E4M3 codes of Q and K, their float32 block scales and V read once, O and lse written once")
-           + f"): {algo:,} B; ratio {hbm / algo:.4f}."]
-    open(os.path.join(pdir, f"{kshort}_{tag}_traffic.md"), "w").write("\n".join(md) + "\n")
-    print(json.dumps({"counters": derived, "hbm_bytes_per_launch": hbm, "algorithmic_bytes": algo}), flush=True)
+    md = [f"# {prefix}, {title} — HBM traffic\n", head, "```", *cmds["traffic"], "```\n",
+          f"Copy calibration ({COPY_MIB} MiB through `{calib['FETCH_SIZE']['copy_kernel']}`): FETCH_SIZE "
+          f"{calib['FETCH_SIZE']['copy_kib']:.1f} KiB/dispatch (n={calib['FETCH_SIZE']['copy_n']}), factor "
+          f"{calib['FETCH_SIZE']['factor']:.4f}; WRITE_SIZE {calib['WRITE_SIZE']['copy_kib']:.1f} KiB/dispatch "
+          f"(n={calib['WRITE_SIZE']['copy_n']}), factor {calib['WRITE_SIZE']['factor']:.4f}.\n",
+          "| kernel | FETCH_SIZE (KiB/dispatch) | WRITE_SIZE (KiB/dispatch) | bytes read | bytes written |",
+          "|---|---|---|---|---|"]
+    for k in spec["kernels"]:
+        t = traffic[k]
+        md.append(f"| `{k}` | {t['FETCH_SIZE']['kib']:.1f} (n={t['FETCH_SIZE']['n']}) | {t['WRITE_SIZE']['kib']:.1f} "
+                  f"(n={t['WRITE_SIZE']['n']}) | {t['FETCH_SIZE']['bytes']:,.0f} | {t['WRITE_SIZE']['bytes']:,.0f} |")
+    md += ["", f"Kernel counts are the mean of each kernel's last {psteps} dispatches.", "",
+           f"HBM traffic per call: {hbm:,.0f} B. Algorithmic bytes ({spec['algo_what']}): {spec['algo']:,} B; "
+           f"ratio {hbm / spec['algo']:.4f}."]
+    open(os.path.join(pdir, f"{prefix}_{tag}_traffic.md"), "w").write("\n".join(md) + "\n")
+    print(json.dumps({"counters": entry, "hbm_bytes_per_launch": hbm, "algorithmic_bytes": spec["algo"]}),
+          flush=True)
 
 
 if __name__ == "__main__":

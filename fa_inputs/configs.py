@@ -118,6 +118,13 @@ class BwdConfig:
         f = 10 * self.B * self.H * self.L * self.L * self.d
         return f // 2 if self.causal else f
 
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Bytes one backward call must move: Q, K, V, O, dO and the float32 lse
+        read once, dQ, dK, dV written once (16-bit storage)."""
+        n = self.B * self.H * self.L
+        return 8 * n * self.d * 2 + 4 * n
+
 
 # Backward shapes.  Seeds 20/21; streams 0/1/2/3 are Q/K/V/dO.
 BWD = [
