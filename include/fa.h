@@ -43,7 +43,7 @@ enum fa_status {
                                  causal not 0/1; B*H*L*d >= 2^62; too many Q tiles for one grid */
     FA_ERR_UNSUPPORTED = -2,  /* d not 64 or 128; unknown dtype                              */
     FA_ERR_ALIGN = -3,        /* q, k, v or o not 16-byte aligned; lse not 4-byte aligned   */
-    FA_ERR_HIP = -4           /* the kernel launch failed; see fa_last_hip_error()          */
+    FA_ERR_HIP = -4           /* a HIP call failed; see fa_last_hip_error()                 */
 };
 
 /*

@@ -581,15 +581,13 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 template <class T, int D, bool CAUSAL>
 int launch_bwd(const BwdParams& p, hipStream_t stream) {
     const long long rows = (long long)p.BH * p.L;
-    hipLaunchKernelGGL((fa_bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p, rows);
-    int rc = fa_detail::launch_status();
+    int rc = fa_detail::launch_kernel(fa_bwd_pre_kernel<T, D>, dim3((unsigned)((rows + 15) / 16)), dim3(256), stream,
+                                      p, rows);
     if (rc != FA_OK) return rc;
     const dim3 grid((unsigned)((long long)p.BH * ((p.L + 127) / 128)));
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
-    rc = fa_detail::launch_status();
+    rc = fa_detail::launch_kernel(fa_bwd_dq_kernel<T, D, CAUSAL>, grid, dim3(256), stream, p);
     if (rc != FA_OK) return rc;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, stream, p);
-    return fa_detail::launch_status();
+    return fa_detail::launch_kernel(fa_bwd_dkdv_kernel<T, D, CAUSAL>, grid, dim3(256), stream, p);
 }
 
 template <class T>

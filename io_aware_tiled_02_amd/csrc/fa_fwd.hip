@@ -54,15 +54,6 @@
 
 namespace fa_detail {
 thread_local int g_last_hip = 0;
-
-int launch_status() {
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) {
-        g_last_hip = (int)err;
-        return FA_ERR_HIP;
-    }
-    return FA_OK;
-}
 }  // namespace fa_detail
 
 namespace {
@@ -1040,8 +1031,6 @@ inline Params make_params(const void* q, const void* k, const void* v, void* o, 
     return p;
 }
 
-inline int launch_status() { return fa_detail::launch_status(); }
-
 template <class T, int D, bool CAUSAL>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int L, float scale,
            hipStream_t stream) {
@@ -1049,14 +1038,13 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     const Params p = make_params(q, k, v, o, lse, BH, L, scale, t.br);
     const long long grid = (long long)BH * p.Tr;
     if constexpr (sizeof(T) == 2) {
-        hipLaunchKernelGGL((fa_fwd_h_kernel<T, D, CAUSAL, false>), dim3((unsigned)grid), dim3(HCfg<D>::NW * 64), 0,
-                           stream, p);
+        return fa_detail::launch_kernel(fa_fwd_h_kernel<T, D, CAUSAL, false>, dim3((unsigned)grid),
+                                        dim3(HCfg<D>::NW * 64), stream, p);
     } else {
         using Ch = F32Choice<T, D>;
-        hipLaunchKernelGGL((fa_fwd_f32_kernel<float, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>), dim3((unsigned)grid),
-                           dim3(Ch::C::NT), 0, stream, p);
+        return fa_detail::launch_kernel(fa_fwd_f32_kernel<float, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>,
+                                        dim3((unsigned)grid), dim3(Ch::C::NT), stream, p);
     }
-    return launch_status();
 }
 
 template <class T>
@@ -1090,9 +1078,8 @@ int check_args(int B, int H, int L, int d, int causal, int dtype) {
 template <class T, int D, bool CAUSAL>
 int launch_fp8(const Params& p, hipStream_t stream) {
     const long long grid = (long long)p.BH * p.Tr;
-    hipLaunchKernelGGL((fa_fwd_h_kernel<T, D, CAUSAL, true>), dim3((unsigned)grid), dim3(HCfg<D, true>::NW * 64), 0,
-                       stream, p);
-    return launch_status();
+    return fa_detail::launch_kernel(fa_fwd_h_kernel<T, D, CAUSAL, true>, dim3((unsigned)grid),
+                                    dim3(HCfg<D, true>::NW * 64), stream, p);
 }
 
 template <class T>
@@ -1166,7 +1153,7 @@ extern "C" const char* fa_strerror(int status) {
         case FA_ERR_ALIGN:
             return "misaligned pointer (q, k, v, o need 16 bytes; lse needs 4)";
         case FA_ERR_HIP:
-            return "HIP kernel launch failed (see fa_last_hip_error)";
+            return "a HIP call failed (see fa_last_hip_error)";
         default:
             return "unknown status";
     }

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void fa_quant_kernel(const char* x, unsigned c
     const int b = blockIdx.x, bh = blockIdx.y;
     const int r0 = b * block, r1 = min(r0 + block, L);
     const long long e0 = ((long long)bh * L + r0) * d;
-    const int n8 = (r1 - r0) * d / 8;             // 16-byte input pieces of the block
+    const long long n8 = (long long)(r1 - r0) * d / 8;   // 16-byte input pieces of the block
     const char* src = x + e0 * 2;
     unsigned char* dst = x8 + e0;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void fa_quant_kernel(const char* x, unsigned c
 #pragma unroll
         for (int p = 0; p < kKeep; ++p) amax = fmaxf(amax, piece_amax<T>(held[p]));
     } else {
-        for (int i = tid; i < n8; i += 256) amax = fmaxf(amax, piece_amax<T>(ld16(src + (long long)i * 16)));
+        for (long long i = tid; i < n8; i += 256) amax = fmaxf(amax, piece_amax<T>(ld16(src + i * 16)));
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void fa_quant_kernel(const char* x, unsigned c
             if (i < n8) quant_store<T>(held[p], s, dst + (long long)i * 8);
         }
     } else {
-        for (int i = tid; i < n8; i += 256) quant_store<T>(ld16(src + (long long)i * 16), s, dst + (long long)i * 8);
+        for (long long i = tid; i < n8; i += 256) quant_store<T>(ld16(src + i * 16), s, dst + i * 8);
     }
 }
 
@@ -112,14 +112,14 @@ extern "C" int fa_quantize_fp8(const void* x, int dtype, int B, int H, int L, in
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H > 65535) return FA_ERR_INVALID_ARG;
+    // one head's tensor must stay below 2 GiB, as for fa_fwd
+    if ((long long)L * d * 2 >= (1LL << 31)) return FA_ERR_INVALID_ARG;
     if (((uintptr_t)x | (uintptr_t)x8) % 16 != 0 || (uintptr_t)scales % 4 != 0) return FA_ERR_ALIGN;
-    const int nblk = (L + block - 1) / block;
+    const long long nblk = ((long long)L + block - 1) / block;     // <= L
     const dim3 grid((unsigned)nblk, (unsigned)(B * H));
     if (dtype == FA_BF16)
-        hipLaunchKernelGGL((fa_quant_kernel<__bf16>), grid, dim3(256), 0, stream, static_cast<const char*>(x),
-                           static_cast<unsigned char*>(x8), scales, L, d, block, nblk);
-    else
-        hipLaunchKernelGGL((fa_quant_kernel<_Float16>), grid, dim3(256), 0, stream, static_cast<const char*>(x),
-                           static_cast<unsigned char*>(x8), scales, L, d, block, nblk);
-    return fa_detail::launch_status();
+        return fa_detail::launch_kernel(fa_quant_kernel<__bf16>, grid, dim3(256), stream, static_cast<const char*>(x),
+                                        static_cast<unsigned char*>(x8), scales, L, d, block, (int)nblk);
+    return fa_detail::launch_kernel(fa_quant_kernel<_Float16>, grid, dim3(256), stream, static_cast<const char*>(x),
+                                    static_cast<unsigned char*>(x8), scales, L, d, block, (int)nblk);
 }

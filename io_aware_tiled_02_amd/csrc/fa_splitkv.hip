@@ -236,8 +236,7 @@ size_t workspace_bytes(long long rows, int d, int nsplit) {
 template <class T, int D, int LQ>
 int launch_split(const SkParams& p, hipStream_t stream) {
     const dim3 grid((unsigned)((p.nsplit + 3) / 4), (unsigned)p.BH);
-    hipLaunchKernelGGL((fa_splitkv_kernel<T, D, LQ>), grid, dim3(256), 0, stream, p);
-    return fa_detail::launch_status();
+    return fa_detail::launch_kernel(fa_splitkv_kernel<T, D, LQ>, grid, dim3(256), stream, p);
 }
 
 template <class T, int D>
@@ -252,9 +251,8 @@ template <class T, int D>
 int launch_combine(const float* opart, const float* lpart, void* o, float* lse, int nsplit, long long rows,
                    hipStream_t stream) {
     const dim3 grid((unsigned)((rows + 3) / 4));
-    hipLaunchKernelGGL((fa_combine_kernel<T, D>), grid, dim3(256), 0, stream, opart, lpart, static_cast<T*>(o), lse,
-                       nsplit, rows);
-    return fa_detail::launch_status();
+    return fa_detail::launch_kernel(fa_combine_kernel<T, D>, grid, dim3(256), stream, opart, lpart, static_cast<T*>(o),
+                                    lse, nsplit, rows);
 }
 
 int dispatch_combine(const float* opart, const float* lpart, void* o, float* lse, int nsplit, long long rows, int d,
@@ -279,37 +277,29 @@ int check_common(int B, int H, int Lq, int d, int dtype) {
     return FA_OK;
 }
 
-}  // namespace
-
-extern "C" size_t fa_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int nsplit) {
-    if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || (d != 64 && d != 128)) return 0;
-    if (nsplit <= 0) nsplit = auto_splits(B, H, Lk);
-    return workspace_bytes((long long)B * H * Lq, d, nsplit);
-}
-
-extern "C" int fa_splitkv_splits(int B, int H, int Lk) {
-    if (B <= 0 || H <= 0 || Lk <= 0) return 0;
-    return auto_splits(B, H, Lk);
-}
-
-extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
-                              int Lk, int d, float scale, int dtype, int nsplit, void* workspace,
-                              size_t workspace_size, hipStream_t stream) {
-    if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_INVALID_ARG;
+// Checks of fa_fwd_splitkv's arguments other than the workspace; fills
+// nsplit (automatic when <= 0) and the partial-result row count.
+int check_splitkv(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H, int Lq,
+                  int Lk, int d, float scale, int dtype, int& nsplit, long long& rows) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     int rc = check_common(B, H, Lq, d, dtype);
     if (rc != FA_OK) return rc;
     if (Lk <= 0) return FA_ERR_INVALID_ARG;
     if (Lq > kMaxLq) return FA_ERR_UNSUPPORTED;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
     if ((long double)B * H * Lk * d >= 4.6e18L) return FA_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
-        !aligned(workspace, 256))
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return FA_ERR_ALIGN;
     if (nsplit <= 0) nsplit = auto_splits(B, H, Lk);
     if (nsplit > 4 * 65535) return FA_ERR_INVALID_ARG;
-    const long long rows = (long long)B * H * Lq;
-    if (workspace_size < workspace_bytes(rows, d, nsplit)) return FA_ERR_INVALID_ARG;
+    rows = (long long)B * H * Lq;
+    return FA_OK;
+}
 
+// The chunk kernel into the partial results at `workspace` (256-byte
+// aligned, workspace_bytes(rows, d, nsplit) long), then the merge.
+int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
+                int d, float scale, int dtype, int nsplit, long long rows, void* workspace, hipStream_t stream) {
     float* opart = static_cast<float*>(workspace);
     float* lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                             ((size_t)nsplit * rows * d * sizeof(float) + 255) / 256 * 256);
@@ -326,6 +316,7 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
     p.chunk = (Lk + nsplit - 1) / nsplit;
     p.c = scale * kLog2e;
 
+    int rc;
     if (dtype == FA_BF16)
         rc = d == 64 ? launch_split_lq<__bf16, 64>(p, stream) : launch_split_lq<__bf16, 128>(p, stream);
     else if (dtype == FA_F16)
@@ -334,6 +325,31 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
         rc = d == 64 ? launch_split_lq<float, 64>(p, stream) : launch_split_lq<float, 128>(p, stream);
     if (rc != FA_OK) return rc;
     return dispatch_combine(opart, lpart, o, lse, nsplit, rows, d, dtype, stream);
+}
+
+}  // namespace
+
+extern "C" size_t fa_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int nsplit) {
+    if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || (d != 64 && d != 128)) return 0;
+    if (nsplit <= 0) nsplit = auto_splits(B, H, Lk);
+    return workspace_bytes((long long)B * H * Lq, d, nsplit);
+}
+
+extern "C" int fa_splitkv_splits(int B, int H, int Lk) {
+    if (B <= 0 || H <= 0 || Lk <= 0) return 0;
+    return auto_splits(B, H, Lk);
+}
+
+extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
+                              int Lk, int d, float scale, int dtype, int nsplit, void* workspace,
+                              size_t workspace_size, hipStream_t stream) {
+    long long rows = 0;
+    const int rc = check_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, rows);
+    if (rc != FA_OK) return rc;
+    if (!workspace) return FA_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
+    if (workspace_size < workspace_bytes(rows, d, nsplit)) return FA_ERR_INVALID_ARG;
+    return run_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, rows, workspace, stream);
 }
 
 extern "C" int fa_combine(const float* o_part, const float* lse_part, int nsplit, int B, int H, int Lq, int d,

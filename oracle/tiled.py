@@ -9,10 +9,12 @@ the plain-definition oracle in fa_oracle.c.
 
 Sources (page title, then the section or item):
   * "04 Transformers, Attention, and FlashAttention": FlashAttention-2
-    Algorithm 1 -- Q blocks outer, K/V blocks inner, running (O~, l, m) with
-    sentinels (0, 0, -inf), m_new = max(m_old, rowmax S), P~ = exp(S - m_new),
+    Algorithm 1 -- Q blocks outer, K/V blocks inner, running (O~, l, m),
+    m_new = max(m_old, rowmax S), P~ = exp(S - m_new),
     l_new = e^(m_old - m_new) l_old + rowsum P~, O~ scaled by e^(m_old - m_new)
-    plus P~ V_j, then one division by l and L = m + log l.
+    plus P~ V_j, then one division by l and L = m + log l.  fa2_forward keeps
+    these in base-2 units and starts the state from the first block instead of
+    from the (0, 0, -inf) sentinels; both give the same numbers.
   * "大语言模型研究14", section 1.1 eqs. (4)-(7) and section 2: the scalar and
     row-block recurrences s_k = e^(m_{k-1} - m_k) s_{k-1} + b_k.
   * "FlashAttention: как реально считается attention на GPU", the online
@@ -46,42 +48,55 @@ def _block_scores(Qi, Kj, scale, causal, rows, cols):
     return S
 
 
+LOG2E = 1.0 / math.log(2.0)
+
+
 def fa2_forward(Q, K, V, scale: float, Br: int, Bc: int, causal: bool = False):
     """FlashAttention-2 order for one head: Q (L, d), K (L, d), V (L, d) float64.
 
-    Returns (O, lse, trace) where trace lists, per Q block, the per-row
-    correction factors applied at each K/V block (for the walk-through pin).
+    The statistics are kept in base-2 units (t = S log2 e, so e^(S - m) is
+    2^(t - m2)), and the first K/V block a Q block visits starts the state
+    (m2, l, acc) outright; every later block folds in with the factor
+    2^(m2_old - m2_new).  The first block always holds key 0, which every row
+    sees (causal or not), so each row's state is finite from the start.
+
+    Returns (O, lse, trace) where trace lists, per Q block, the per-row factor
+    applied to the carried state at each K/V block (0 at the first block,
+    where nothing is carried).
     """
     L, d = Q.shape
-    Tr = math.ceil(L / Br)
-    Tc = math.ceil(L / Bc)
     O = np.empty((L, d))
     lse = np.empty(L)
     trace = []
-    for i in range(Tr):
-        r0, r1 = i * Br, min((i + 1) * Br, L)
+    for r0 in range(0, L, Br):
+        r1 = min(r0 + Br, L)
         rows = np.arange(r0, r1)
         Qi = Q[r0:r1]
-        acc = np.zeros((r1 - r0, d))      # unnormalised output
-        l = np.zeros(r1 - r0)             # running sum
-        m = np.full(r1 - r0, -np.inf)     # running maximum
-        corr_i = []
-        for j in range(Tc):
-            c0, c1 = j * Bc, min((j + 1) * Bc, L)
-            if causal and c0 > r1 - 1:
-                break                     # block entirely after every query row
-            cols = np.arange(c0, c1)
-            S = _block_scores(Qi, K[c0:c1], scale, causal, rows, cols)
-            m_new = np.maximum(m, S.max(axis=1))
-            P = np.exp(S - m_new[:, None])
-            alpha = _correction(m, m_new)
-            l = alpha * l + P.sum(axis=1)
-            acc = alpha[:, None] * acc + P @ V[c0:c1]
-            m = m_new
-            corr_i.append(alpha)
+        # causal: K/V blocks starting after the block's last row are skipped
+        last = r1 - 1 if causal else L - 1
+        factors = []
+        for c0 in range(0, last + 1, Bc):
+            c1 = min(c0 + Bc, L)
+            T = _block_scores(Qi, K[c0:c1], scale, causal, rows, np.arange(c0, c1)) * LOG2E
+            bmax = T.max(axis=1)
+            if c0 == 0:
+                assert np.all(np.isfinite(bmax)), "every row sees key 0"
+                m2 = bmax
+                P = np.exp2(T - m2[:, None])
+                l = P.sum(axis=1)
+                acc = P @ V[c0:c1]
+                factors.append(np.zeros(r1 - r0))
+                continue
+            m2_new = np.maximum(m2, bmax)           # finite: m2 is
+            a = np.exp2(m2 - m2_new)
+            P = np.exp2(T - m2_new[:, None])        # masked scores give 0
+            l = a * l + P.sum(axis=1)
+            acc = a[:, None] * acc + P @ V[c0:c1]
+            m2 = m2_new
+            factors.append(a)
         O[r0:r1] = acc / l[:, None]
-        lse[r0:r1] = m + np.log(l)
-        trace.append(corr_i)
+        lse[r0:r1] = (m2 + np.log2(l)) / LOG2E
+        trace.append(factors)
     return O, lse, trace
 
 

@@ -41,6 +41,19 @@ def test_generator_library_exports_every_declared_function():
         assert hasattr(lib, n), f"{n} declared in include/fa_gen.h but not exported"
 
 
+def test_binding_binds_only_declared_and_exported_functions():
+    """Every C function the Python binding declares argument types for is
+    declared in include/fa.h and exported by the built library."""
+    src = open(os.path.join(ROOT, "io_aware_tiled_02_amd", "__init__.py")).read()
+    bound = set(re.findall(r"lib\.(fa_\w+)\.argtypes", src))
+    declared = _declared_functions("fa.h")
+    assert bound, "no bound functions found"
+    assert bound == declared, f"bound but not declared: {bound - declared}; declared but not bound: {declared - bound}"
+    lib = fa.load()
+    for n in bound:
+        assert hasattr(lib, n), f"{n} bound by the binding but not exported"
+
+
 def test_strerror_total():
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
@@ -194,6 +207,8 @@ def _qz(**kw):
     (dict(x=A + 8), fa.FA_ERR_ALIGN),
     (dict(x8=A + 4), fa.FA_ERR_ALIGN),
     (dict(sc=A + 2), fa.FA_ERR_ALIGN),
+    (dict(L=1 << 23), fa.FA_ERR_INVALID_ARG),   # one head's tensor of 2 GiB: L*d*2 >= 2^31
+    (dict(L=1 << 24, d=64), fa.FA_ERR_INVALID_ARG),
 ])
 def test_quantize_fp8_argument_errors(kw, want):
     assert _qz(**kw) == want

@@ -121,3 +121,52 @@ def test_fp8_repeat_overwrite_side_stream(causal):
     o_ref, lse_ref = oracle.fwd_fp8(r8q, r8k, rsq, rsk, vn, gen.BF16, 0.1, causal, 128, 64)
     compare_fp8(to_host64(out, gen.BF16), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref,
                 lse_tolerance(d, 0.1, rsq, rsk), f"fp8 side stream causal={causal}")
+
+
+def test_pending_error_of_another_call_is_not_reported():
+    """A HIP error left pending on the thread by an unrelated call (here
+    hipErrorNotReady from hipStreamQuery on a busy stream, when this HIP
+    records it) is not reported by the library's launches: fa_fwd and fa_bwd
+    return FA_OK and write correct results."""
+    import ctypes
+    import torch
+    import io_aware_tiled_02_amd as fa
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipStreamQuery.argtypes = [ctypes.c_void_p]
+    hip.hipStreamQuery.restype = ctypes.c_int
+    hip.hipPeekAtLastError.restype = ctypes.c_int
+    hip.hipGetLastError.restype = ctypes.c_int
+    B, H, L, d = 1, 2, 300, 128
+    say("[behaviour] fa_fwd / fa_bwd after a pending hipErrorNotReady")
+    qn, kn, vn, gn = (gen.fill(gen.BF16, (B, H, L, d), 74, s) for s in range(4))
+    q, k, v, g = (to_device(x, gen.BF16) for x in (qn, kn, vn, gn))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, L), dtype=torch.uint8, device="cuda")
+    outs = [torch.full_like(q, float("nan")) for _ in range(3)]
+    # a busy stream: a long forward pass, queried at once
+    big = [torch.zeros((1, 32, 8192, 128), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    big_o = torch.empty_like(big[0])
+    big_l = torch.empty((1, 32, 8192), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    hip.hipGetLastError()
+    rc = fa.fa_fwd(big[0].data_ptr(), big[1].data_ptr(), big[2].data_ptr(), big_o.data_ptr(), big_l.data_ptr(),
+                   1, 32, 8192, 128, 0.1, 0, gen.BF16, s.cuda_stream)
+    assert rc == 0
+    q_rc = hip.hipStreamQuery(ctypes.c_void_p(s.cuda_stream))
+    pending = hip.hipPeekAtLastError()
+    rc_f = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, L, d, 0.125, 0,
+                     gen.BF16, s.cuda_stream)
+    rc_b = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), g.data_ptr(),
+                     outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), B, H, L, d, 0.125, 0, gen.BF16,
+                     ws.data_ptr(), ws.numel(), s.cuda_stream)
+    after = hip.hipPeekAtLastError()
+    torch.cuda.synchronize()
+    hip.hipGetLastError()
+    say(f"[behaviour] hipStreamQuery -> {q_rc}, pending before {pending}, after {after}; fa_fwd {rc_f}, fa_bwd {rc_b}")
+    assert rc_f == 0 and rc_b == 0, f"fa_fwd {rc_f}, fa_bwd {rc_b} with a pending error {pending}"
+    o_ref, lse_ref = oracle.fwd(qn, kn, vn, gen.BF16, 0.125, 0)
+    compare(to_host64(o, gen.BF16), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, gen.BF16, "pending error")
+    ref = oracle.bwd(qn, kn, vn, gn, gen.BF16, 0.125, 0)
+    compare_grads([to_host64(x, gen.BF16) for x in outs], ref, "pending error")

@@ -7,7 +7,7 @@
   oracle.fwd_fp8.
 * both FP8 shapes at full size in the launch the bench times (GPU quantiser,
   then the FP8 forward): codes bit-exact on every element, O and lse on
-  sampled rows of sampled heads.
+  every row of every head.
 
 Tolerances.  O: max-abs 2e-2, mean-abs 2e-3, as for the 16-bit forward.
 lse: 1e-3 plus the score error of the FP8 matrix core.  gfx950's
@@ -194,14 +194,12 @@ def test_fp8_workload(ci):
     assert np.array_equal(skd.cpu().numpy().view(np.uint32), sk.view(np.uint32))
     o = to_host64(o, cfg.dtype)
     lse = lse.cpu().numpy().astype(np.float64)
-    rows = gen.sample_rows(cfg.L, cfg.check_rows, cfg.seed)
-    nbq, nbk = sq.shape[1], sk.shape[1]
-    for (b, h) in [(0, 0), (cfg.B - 1, cfg.H // 2 + 1), (cfg.B - 1, cfg.H - 1)]:
-        bh = b * cfg.H + h
-        o_ref, lse_ref = oracle.fwd_fp8(_head(q8, b, h), _head(k8, b, h), sq[bh:bh + 1], sk[bh:bh + 1],
-                                        _head(v, b, h), cfg.dtype, cfg.scale, cfg.causal, cfg.block_q,
-                                        cfg.block_k, rows=rows)
-        stats = compare_fp8(o[b:b + 1, h:h + 1, rows], lse[b:b + 1, h:h + 1, rows], o_ref, lse_ref,
-                            lse_tolerance(cfg.d, cfg.scale, sq[bh], sk[bh]), f"{cfg.name} b={b} h={h}")
-        say(f"[fp8-full] b={b} h={h}: {stats}")
-        assert nbq and nbk
+    # every row of every head, against the oracle on the oracle's own codes
+    o_ref, lse_ref = oracle.fwd_fp8(q8, k8, sq, sk, v, cfg.dtype, cfg.scale, cfg.causal, cfg.block_q, cfg.block_k)
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            bh = b * cfg.H + h
+            stats = compare_fp8(o[b, h], lse[b, h], o_ref[b, h], lse_ref[b, h],
+                                lse_tolerance(cfg.d, cfg.scale, sq[bh], sk[bh]), f"{cfg.name} b={b} h={h}")
+            if h in (0, cfg.H - 1):
+                say(f"[fp8-full] b={b} h={h}: {stats}")

@@ -78,22 +78,16 @@ def test_splitkv_peaked_and_long(sigma):
     compare(o, lse, o_ref, lse_ref, dtype, f"peaked sigma={sigma}")
 
 
-def test_splitkv_decode_workload_sampled():
+def test_splitkv_decode_workload():
     """The decoding workload at full size (B8 H32 Lq1 Lk16384 d128 bf16), the
-    launch the bench times (automatic nsplit), checked on 24 sampled heads."""
+    launch the bench times (automatic nsplit), checked on every head."""
     cfg = gen.DECODE
     say(f"[splitkv] workload {cfg.name}")
     q, k, v = gen.make_decode_qkv(cfg)
     o, lse = _run_splitkv(q, k, v, cfg.dtype, cfg.scale, 0)
-    heads = gen.sample_rows(cfg.B * cfg.H, 24, cfg.seed)
-    qs = q.reshape(cfg.B * cfg.H, 1, cfg.Lq, cfg.d)[heads]
-    ks = k.reshape(cfg.B * cfg.H, 1, cfg.Lk, cfg.d)[heads]
-    vs = v.reshape(cfg.B * cfg.H, 1, cfg.Lk, cfg.d)[heads]
-    o_ref, lse_ref = oracle.attn_range(qs, ks, vs, cfg.dtype, cfg.scale, 0, cfg.Lk)
-    o_s = o.reshape(cfg.B * cfg.H, 1, cfg.Lq, cfg.d)[heads]
-    l_s = lse.reshape(cfg.B * cfg.H, 1, cfg.Lq)[heads]
-    say(f"[splitkv] checked heads {heads.tolist()}")
-    compare(o_s, l_s, o_ref, lse_ref, cfg.dtype, cfg.name)
+    o_ref, lse_ref = oracle.attn_range(q, k, v, cfg.dtype, cfg.scale, 0, cfg.Lk)
+    stats = compare(o, lse, o_ref, lse_ref, cfg.dtype, cfg.name)
+    say(f"[splitkv] all {cfg.B * cfg.H} heads: {stats}")
 
 
 @pytest.mark.parametrize("dtype", [gen.BF16, gen.F16, gen.F32])
