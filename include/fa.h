@@ -43,7 +43,9 @@ enum fa_status {
                                  causal not 0/1; B*H*L*d >= 2^62; too many Q tiles for one grid */
     FA_ERR_UNSUPPORTED = -2,  /* d not 64 or 128; unknown dtype                              */
     FA_ERR_ALIGN = -3,        /* q, k, v or o not 16-byte aligned; lse not 4-byte aligned   */
-    FA_ERR_HIP = -4           /* a HIP call failed; see fa_last_hip_error()                 */
+    FA_ERR_HIP = -4,          /* a HIP call failed; see fa_last_hip_error()                 */
+    FA_ERR_SCRATCH = -5       /* fa_fwd_splitkv_noalloc: the partial results would exceed
+                                 FA_NOALLOC_SCRATCH_BYTES                                   */
 };
 
 /*
@@ -151,6 +153,37 @@ size_t fa_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int nspli
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int Lq, int Lk, int d, float scale, int dtype, int nsplit,
                    void* workspace, size_t workspace_size, hipStream_t stream);
+
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory
+ * around the call (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Same arguments (minus workspace and workspace_size), same kernels and
+ * bit-identical results as fa_fwd_splitkv.  The partial results live in a
+ * device array of FA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU
+ * it runs on, from that GPU's first call until the process ends.  The GPU is
+ * the stream's (the current device for the null stream); the first call on a
+ * GPU looks the array's address up (hipGetSymbolAddress, with that GPU made
+ * current for the lookup and the caller's current device restored).  The call
+ * makes no hipMalloc, hipFree or other allocating call.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap on a GPU
+ * (different streams, or different host threads, without ordering between
+ * them) race and give undefined results.  Calls ordered on one stream are
+ * safe.  Nothing in the array needs clearing between calls: every call writes
+ * each partial result before its merge reads it.
+ *
+ * Errors as for fa_fwd_splitkv; FA_ERR_SCRATCH when
+ * fa_splitkv_workspace_bytes(B, H, Lq, Lk, d, nsplit) > FA_NOALLOC_SCRATCH_BYTES
+ * (pass a smaller nsplit, or use fa_fwd_splitkv); FA_ERR_HIP when the stream's
+ * device or the array's address cannot be obtained.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Lq, int Lk, int d, float scale, int dtype, int nsplit,
+                           hipStream_t stream);
 
 /*
  * fa_combine -- enqueue only the merge of nsplit partial results.

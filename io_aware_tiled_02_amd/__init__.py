@@ -12,7 +12,9 @@ import ctypes
 import os
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_HIP = 0, -1, -2, -3, -4
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+# size of the device array behind fa_fwd_splitkv_noalloc (include/fa.h)
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
 _lib = None
@@ -47,6 +49,8 @@ def load():
         lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
         lib.fa_fwd_splitkv.restype = i
+        lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+        lib.fa_fwd_splitkv_noalloc.restype = i
         lib.fa_combine.argtypes = [vp, vp, i, i, i, i, i, vp, vp, i, vp]
         lib.fa_combine.restype = i
         lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
@@ -79,6 +83,12 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, works
     """The C entry point as is (raw device addresses and stream handle)."""
     return load().fa_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, workspace,
                                  workspace_size, stream)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, stream) -> int:
+    """The C entry point as is (raw device addresses and stream handle); the
+    partial results go to the library's own per-GPU scratch array."""
+    return load().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, stream)
 
 
 def fa_combine(o_part, lse_part, nsplit, B, H, Lq, d, o, lse, dtype, stream) -> int:

@@ -1154,6 +1154,8 @@ extern "C" const char* fa_strerror(int status) {
             return "misaligned pointer (q, k, v, o need 16 bytes; lse needs 4)";
         case FA_ERR_HIP:
             return "a HIP call failed (see fa_last_hip_error)";
+        case FA_ERR_SCRATCH:
+            return "the partial results exceed the library's no-allocation scratch (FA_NOALLOC_SCRATCH_BYTES)";
         default:
             return "unknown status";
     }

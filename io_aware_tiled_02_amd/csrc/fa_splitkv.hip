@@ -31,6 +31,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -327,6 +329,42 @@ int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse
     return dispatch_combine(opart, lpart, o, lse, nsplit, rows, d, dtype, stream);
 }
 
+// ---- the library's own scratch for fa_fwd_splitkv_noalloc ----
+//
+// One array per GPU, allocated with the code object when the library is first
+// used on that GPU and held until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: kernels get the device
+// address that hipGetSymbolAddress returns for the current device, looked up
+// once per device and kept in g_scratch.
+constexpr int kMaxDevices = 64;
+static __device__ __attribute__((aligned(256))) char scratch[FA_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// Device address of `scratch` on `dev`, with `dev` made current for the
+// lookup (and the caller's current device restored).
+int scratch_on(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int cur = -1;
+        hipError_t err = hipGetDevice(&cur);
+        if (err != hipSuccess) return fa_detail::status_of(err);
+        if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess) return fa_detail::status_of(err);
+        void* ptr = nullptr;
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (err == hipSuccess) err = back;
+        }
+        if (err != hipSuccess) return fa_detail::status_of(err);
+        if (ptr == nullptr || (uintptr_t)ptr % 256 != 0) return fa_detail::status_of(hipErrorInvalidSymbol);
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" size_t fa_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int nsplit) {
@@ -350,6 +388,22 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
     if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
     if (workspace_size < workspace_bytes(rows, d, nsplit)) return FA_ERR_INVALID_ARG;
     return run_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, rows, workspace, stream);
+}
+
+extern "C" int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                      int Lq, int Lk, int d, float scale, int dtype, int nsplit, hipStream_t stream) {
+    long long rows = 0;
+    int rc = check_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, rows);
+    if (rc != FA_OK) return rc;
+    if (workspace_bytes(rows, d, nsplit) > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    // the GPU the work runs on: the stream's, or the current one for the null stream
+    int dev = -1;
+    const hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (err != hipSuccess) return fa_detail::status_of(err);
+    void* ws = nullptr;
+    rc = scratch_on(dev, &ws);
+    if (rc != FA_OK) return rc;
+    return run_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, dtype, nsplit, rows, ws, stream);
 }
 
 extern "C" int fa_combine(const float* o_part, const float* lse_part, int nsplit, int B, int H, int Lq, int d,

@@ -55,7 +55,7 @@ def test_binding_binds_only_declared_and_exported_functions():
 
 
 def test_strerror_total():
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
 
 
@@ -127,6 +127,47 @@ def _sk(**kw):
 ])
 def test_splitkv_argument_errors(kw, want):
     assert _sk(**kw) == want
+
+
+def _skn(**kw):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=4, Lq=1, Lk=1000, d=128, scale=0.1, dtype=2, nsplit=4, stream=0)
+    a.update(kw)
+    return fa.fa_fwd_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Lq"], a["Lk"],
+                                     a["d"], a["scale"], a["dtype"], a["nsplit"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Lk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Lq=9), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(B=300, H=300), fa.FA_ERR_INVALID_ARG),
+    (dict(nsplit=4 * 65535 + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(o=A + 8), fa.FA_ERR_ALIGN),
+    # partial results beyond the library's scratch array: 16 x 2048 x 8 rows x 129 floats > 16 MiB
+    (dict(B=16, H=2048, Lq=8, Lk=100000, nsplit=16), fa.FA_ERR_SCRATCH),
+])
+def test_splitkv_noalloc_argument_errors(kw, want):
+    assert _skn(**kw) == want
+
+
+def test_splitkv_noalloc_scratch_limit():
+    """The size rule: accepted exactly when fa_splitkv_workspace_bytes fits
+    FA_NOALLOC_SCRATCH_BYTES (checked on the host before any HIP call)."""
+    cap = fa.FA_NOALLOC_SCRATCH_BYTES
+    # d = 128, Lq = 1: workspace = pad256(n*128*4) + pad256(n*4) with n = nsplit * B * H
+    n_fit = None
+    for n in range(cap // 516 - 4, cap // 516 + 4):
+        need = ((n * 512 + 255) // 256) * 256 + ((n * 4 + 255) // 256) * 256
+        if need <= cap:
+            n_fit = n
+    assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 10 ** 8, 128, n_fit) <= cap
+    assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 10 ** 8, 128, n_fit + 1) > cap
+    assert _skn(B=1, H=1, Lk=10 ** 8, nsplit=n_fit + 1) == fa.FA_ERR_SCRATCH
 
 
 def test_splitkv_workspace_size_and_auto_splits():
