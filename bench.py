@@ -79,6 +79,42 @@ def traffic_for(workload):
     return w["hbm_bytes_per_launch"] if w else None
 
 
+# VALU issue model of the MI355X SIMD for the softmax roofline: a wave64
+# non-transcendental VALU instruction takes 2 SIMD cycles at the chip's fp32
+# vector peak (157.3 TFLOP/s = 256 CUs x 4 SIMDs x 2.4 GHz x 32 FMA lanes);
+# transcendentals (v_exp_f32, v_log_f32, ...) run at a quarter of that rate.
+VALU_CYCLES, TRANS_CYCLES = 2.0, 8.0
+SIMDS, ENGINE_GHZ = 1024, 2.4
+
+
+def valu_roofline(workload, ms_per_launch):
+    """The kernel's VALU work (SQ_INSTS_VALU minus MFMA, SQ_INSTS_VALU_TRANS_F32
+    per wave, from the counter record of the current source) priced at the
+    issue model above, against the measured launch time: the fraction of the
+    VALU issue bound the kernel reaches.  None without a record."""
+    w = _record("counters", workload)
+    if not w or "per_wave" not in w or not w.get("waves") or not ms_per_launch:
+        return None
+    pw = w["per_wave"]
+    valu = pw["valu"] - pw["mfma"]
+    trans = pw["v_exp_f32"]
+    cycles = (valu - trans) * VALU_CYCLES + trans * TRANS_CYCLES
+    t_ms = w["waves"] * cycles / (SIMDS * ENGINE_GHZ * 1e9) * 1e3
+    return {
+        "bound": "alu",
+        "achieved": t_ms / ms_per_launch,
+        "peak": 1.0,
+        "unit": "fraction of the VALU issue bound",
+        "frac": t_ms / ms_per_launch,
+        "valu_bound_ms": t_ms,
+        "valu_per_wave": valu,
+        "trans_per_wave": trans,
+        "waves": w["waves"],
+        "model": f"non-transcendental VALU {VALU_CYCLES:g} and transcendental {TRANS_CYCLES:g} SIMD cycles per "
+                 f"wave64 instruction, {SIMDS} SIMDs at {ENGINE_GHZ} GHz",
+    }
+
+
 def counters_for(workload, ms_per_launch):
     """SQ-counter figures of the workload's kernels (rocprofv3 --pmc runs made by
     --collect-counters), if they were taken on the current kernel sources; with
@@ -467,6 +503,7 @@ def bench_fp8(args, torch, fa, cfg):
             "per_launch_flops": cfg.flops,
             "avg_launch_ms": ms_attn,
         },
+        "roofline_valu": valu_roofline(args.workload, ms_attn),
         "counters": counters_for(args.workload, ms_attn),
         "cpu_baseline": None,
     }
@@ -612,6 +649,7 @@ def main():
             "pct_of_peak": 100.0 * tflops / peak,
         },
         "roofline": roofline,
+        "roofline_valu": valu_roofline(cfg.index, ms),
         "counters": counters_for(cfg.index, ms),
         "cpu_baseline": None,
     }
@@ -853,6 +891,7 @@ def summarize_counters(args):
             "trace_avg_ms": float(_col(q["st"], "AverageNs", "Average_Ns")) * 1e-6,
             "trace_timed_ms": sum(q["durs"]) / len(q["durs"]) * 1e-6,
             "hbm_bytes_per_launch": hbm_k,
+            "waves": sq["SQ_WAVES"],
         }
     hbm = sum(derived[k]["hbm_bytes_per_launch"] for k in spec["kernels"])
     prefix = spec["prefix"]
@@ -911,6 +950,12 @@ def summarize_counters(args):
                f"co-issue {d_['mfma_valu_coexec']:.3f}; LDS busy ≈ {d_['lds_busy']:.3f} of CU cycles, bank-conflict "
                f"cycles {d_['lds_bank_conflict_cycles']:.0f}; HBM {d_['hbm_gbps_under_counters']:.0f} GB/s; per wave: "
                + ", ".join(f"{n} {v:.0f}" for n, v in d_["per_wave"].items())]
+        pw = d_["per_wave"]
+        nv, nt = pw["valu"] - pw["mfma"], pw["v_exp_f32"]
+        tv = d_["waves"] * ((nv - nt) * VALU_CYCLES + nt * TRANS_CYCLES) / (SIMDS * ENGINE_GHZ * 1e9) * 1e3
+        md += [f"  - VALU issue bound of `{k}` ({nv:.0f} VALU instructions per wave besides MFMA, {nt:.0f} of them "
+               f"transcendental; {VALU_CYCLES:g} / {TRANS_CYCLES:g} SIMD cycles per wave64 instruction, {SIMDS} SIMDs at "
+               f"{ENGINE_GHZ} GHz): {tv:.4f} ms, {tv / d_['duration_ms_under_counters']:.3f} of the duration under counters"]
     open(os.path.join(pdir, f"{prefix}_{tag}_sq_counters.md"), "w").write("\n".join(md) + "\n")
 
     md = [f"# {prefix}, {title} — HBM traffic\n", head, "```", *cmds["traffic"], "```\n",

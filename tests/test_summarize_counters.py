@@ -121,6 +121,7 @@ def test_summarize_counters_on_synthetic_output(tmp_path, wl):
         assert d["engine_clock_ghz"] == pytest.approx(CLOCK_GHZ, rel=1e-9)
         assert d["mfma_busy"] == pytest.approx(MFMA_BUSY, rel=1e-9)
         assert d["duration_ms_under_counters"] == pytest.approx(DUR_NS * 1e-6)
+        assert d["waves"] == 8192
     for suffix in ("kernel_trace", "sq_counters", "traffic"):
         assert (out / f"{spec['prefix']}_{spec['tag']}_{suffix}.md").exists()
     rec = json.load(open(out / os.path.basename(bench._record_path("traffic", spec["family"]))))
