@@ -35,7 +35,10 @@
 //  * fp32 (fa_fwd_f32_kernel): 4 waves, K/V staged through registers into
 //    LDS, V written transposed with the 32-key sub-tile's key positions
 //    permuted so each lane's 8 keys are one contiguous 16-byte read;
-//    v_mfma_f32_32x32x2f32 and P kept in fp32.
+//    v_mfma_f32_32x32x2f32 and P kept in fp32.  On grids too small to fill
+//    the chip (d = 64), 8 waves share one 32-row query tile and divide its
+//    keys, each keeping its own (m, l, O); the partial states are merged in
+//    LDS at the end, as split-K/V partials are.
 //  * 16-byte LDS chunks are XOR-swizzled by row to spread banks.
 //  * Workgroups are renumbered so that every query tile of a head runs on the
 //    same XCD (they share that head's K/V in the XCD's L2); causal tiles are
@@ -138,19 +141,35 @@ __device__ inline void work_tile(const Params& p, int& bh, int& qt) {
     }
 }
 
-template <class T, int D, bool CAUSAL, int NQB, int NW, int NKB>
+// SPLIT (small grids): the NW waves share one 32-row query tile and split its
+// keys instead of its rows.  Wave w takes the key tiles w, w + NW, ... with
+// its own K/V staging in LDS and its own running (m, l, O) over those keys;
+// at the end the NW partial states are merged through LDS the way split-K/V
+// partials are (each rescaled by exp of its max minus the overall max).
+template <class T, int D, bool CAUSAL, int NQB, int NW, int NKB, bool SPLIT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(NQB == 1 ? 2 : 1, NQB == 1 ? 2 : 1)))
 void fa_fwd_f32_kernel(Params p) {
     using C = Cfg<T, D, CAUSAL, NQB, NW, NKB>;
+    // staging: the whole workgroup fills one tile, or (SPLIT) each wave its own
+    using CS = std::conditional_t<SPLIT, Cfg<T, D, CAUSAL, NQB, 1, NKB>, C>;
     using frag = typename Ty<T>::frag;
     constexpr int E = C::E;
     constexpr int BC = C::BC;
+    constexpr int BR = SPLIT ? C::QPW : C::BR;
+    static_assert(!SPLIT || NQB == 1, "split keys: one query block per wave");
+    constexpr int SMEM = SPLIT ? NW * CS::STAGE : 2 * C::STAGE;
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     int bh, qt;
-    work_tile<CAUSAL>(p, bh, qt);
+    if constexpr (SPLIT) {
+        bh = blockIdx.x / p.Tr;
+        qt = blockIdx.x % p.Tr;
+    } else {
+        work_tile<CAUSAL>(p, bh, qt);
+    }
 
     const int L = p.L;
     const int tid = threadIdx.x;
@@ -158,14 +177,15 @@ void fa_fwd_f32_kernel(Params p) {
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hf = lane >> 5;
+    const int sid = SPLIT ? lane : tid;               // index among the threads that stage a tile
     const long long head = (long long)bh * L * D;   // element offset of this head
     const char* qh = p.q + head * E;
     const char* kh = p.k + head * E;
     const char* vh = p.v + head * E;
 
-    const int q0 = qt * C::BR;
-    const int qw = q0 + wave * C::QPW;                 // first query row of this wave
-    const int qend = min(q0 + C::BR, L);
+    const int q0 = qt * BR;
+    const int qw = SPLIT ? q0 : q0 + wave * C::QPW;   // first query row of this wave
+    const int qend = min(q0 + BR, L);
     const int ntiles = CAUSAL ? (qend + BC - 1) / BC : (L + BC - 1) / BC;
 
     // ---- Q fragments: B operand of S^T = K Q^T, lane = query, 8 d-values ----
@@ -186,45 +206,46 @@ void fa_fwd_f32_kernel(Params p) {
     }
 
     // ---- K/V tile prefetch registers ----
-    u32x4 kr[C::KPT];
-    u32x4 vr[C::VPT][4];
+    u32x4 kr[CS::KPT];
+    u32x4 vr[CS::VPT][4];
 
     auto fetch = [&](int j) {
         const int kb = j * BC;
 #pragma unroll
-        for (int x = 0; x < C::KPT; ++x) {
-            const int u = tid + x * C::NT;
+        for (int x = 0; x < CS::KPT; ++x) {
+            const int u = sid + x * CS::NT;
             const int row = u / C::KCPR, c = u % C::KCPR;
             const int key = kb + row;
             kr[x] = u32x4{0, 0, 0, 0};
             if (key < L) kr[x] = ld16(kh + ((long long)key * D) * E + 16 * c);
         }
 #pragma unroll
-        for (int x = 0; x < C::VPT; ++x) {
-            const int u = tid + x * C::NT;
+        for (int x = 0; x < CS::VPT; ++x) {
+            const int u = sid + x * CS::NT;
             const int a = u / C::KCPR, c = u % C::KCPR;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int key = kb + 4 * a + e;
                 vr[x][e] = u32x4{0, 0, 0, 0};
-                if (u < C::VUNITS && key < L) vr[x][e] = ld16(vh + ((long long)key * D) * E + 16 * c);
+                if (u < CS::VUNITS && key < L) vr[x][e] = ld16(vh + ((long long)key * D) * E + 16 * c);
             }
         }
     };
 
+    // (SPLIT: stage is the wave)
     auto stash = [&](int stage) {
-        char* ks = smem + stage * C::STAGE;
+        char* ks = smem + stage * CS::STAGE;
         char* vs = ks + C::KBYTES;
 #pragma unroll
-        for (int x = 0; x < C::KPT; ++x) {
-            const int u = tid + x * C::NT;
+        for (int x = 0; x < CS::KPT; ++x) {
+            const int u = sid + x * CS::NT;
             const int row = u / C::KCPR, c = u % C::KCPR;
             st16(ks + row * (D * E) + ((c ^ (row & C::KSW)) * 16), kr[x]);
         }
 #pragma unroll
-        for (int x = 0; x < C::VPT; ++x) {
-            const int u = tid + x * C::NT;
-            if (u >= C::VUNITS) continue;
+        for (int x = 0; x < CS::VPT; ++x) {
+            const int u = sid + x * CS::NT;
+            if (u >= CS::VUNITS) continue;
             const int a = u / C::KCPR, c = u % C::KCPR;
             const int key4 = 4 * a;                             // 4 consecutive keys
             const int pos = (key4 & ~31) | vpos(key4 & 31);     // their position (contiguous 4)
@@ -266,16 +287,9 @@ void fa_fwd_f32_kernel(Params p) {
             for (int r = 0; r < 16; ++r) oacc[qb][dt][r] = 0.f;
     }
 
-    fetch(0);
-    stash(0);
-    __syncthreads();
-
-    for (int j = 0; j < ntiles; ++j) {
-        if (j + 1 < ntiles) fetch(j + 1);
-
-        const char* ks = smem + (j & 1) * C::STAGE;
+    // one K/V tile (keys kb ..) from the staged copy at ks
+    auto tile = [&](const char* ks, int kb) {
         const char* vs = ks + C::KBYTES;
-        const int kb = j * BC;
         // a wave whose rows all precede this tile has nothing to do in it
         const bool active = !CAUSAL || kb <= qw + C::QPW - 1;
         const bool need_mask = (kb + BC > L) || (CAUSAL && kb + BC - 1 > qw);
@@ -385,8 +399,80 @@ void fa_fwd_f32_kernel(Params p) {
                 }
         }
 
-        if (j + 1 < ntiles) stash((j + 1) & 1);
+    };
+
+    // SPLIT: merge the waves' partial states.  Wave w leaves its unnormalised
+    // O_w (32 rows x D), its exponent reference m_w and its sum l_w; with M the
+    // largest m_w of the waves that saw a key (l_w > 0),
+    //     O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w,
+    //     lse = ln2 * (M + log2 sum_w 2^(m_w - M) l_w).
+    auto merge_split = [&]() {
+        if constexpr (SPLIT) {
+            __syncthreads();                                  // every wave is done with its stage
+            float* mo = reinterpret_cast<float*>(smem);       // [NW][32][D]
+            float* mm = mo + NW * 32 * D;                     // [NW][32]
+            float* ml = mm + NW * 32;                         // [NW][32]
+            static_assert((NW * 32 * D + 2 * NW * 32) * 4 <= SMEM, "merge fits the stages");
+            const float ltot = lsum[0] + __shfl_xor(lsum[0], 32);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    mo[(wave * 32 + l32) * D + dt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)] = oacc[0][dt][r];
+            if (hf == 0) {
+                mm[wave * 32 + l32] = mc[0];
+                ml[wave * 32 + l32] = ltot;
+            }
+            __syncthreads();
+            // thread t: row t / (D/4), columns 4*(t % (D/4)) .. +3
+            for (int t = tid; t < 32 * (D / 4); t += NW * 64) {
+                const int r = t / (D / 4), c0 = 4 * (t % (D / 4));
+                const int query = q0 + r;
+                if (query >= L) continue;
+                float M = -INFINITY;
+                for (int w = 0; w < NW; ++w)
+                    if (ml[w * 32 + r] > 0.f) M = fmaxf(M, mm[w * 32 + r]);
+                float lt = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int w = 0; w < NW; ++w) {
+                    const float lw = ml[w * 32 + r];
+                    if (!(lw > 0.f)) continue;
+                    const float f = __builtin_amdgcn_exp2f(mm[w * 32 + r] - M);
+                    lt += f * lw;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] += f * mo[(w * 32 + r) * D + c0 + e];
+                }
+                const float inv = 1.f / lt;
+                float o4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] = acc[e] * inv;
+                st16(p.o + (head + (long long)query * D + c0) * E, __builtin_bit_cast(u32x4, o4));
+                if (c0 == 0) p.lse[(long long)bh * L + query] = (M + __builtin_amdgcn_logf(lt)) * kLn2;
+            }
+        }
+    };
+
+    if constexpr (SPLIT) {
+        // each wave streams its own tiles: the next one's loads are in flight
+        // while the current one is computed (a wave's LDS accesses complete
+        // in order, so its stage needs no barrier)
+        if (wave < ntiles) fetch(wave);
+        for (int j = wave; j < ntiles; j += NW) {
+            stash(wave);
+            if (j + NW < ntiles) fetch(j + NW);
+            tile(smem + wave * CS::STAGE, j * BC);
+        }
+        merge_split();
+        return;
+    } else {
+        fetch(0);
+        stash(0);
         __syncthreads();
+        for (int j = 0; j < ntiles; ++j) {
+            if (j + 1 < ntiles) fetch(j + 1);
+            tile(smem + (j & 1) * C::STAGE, j * BC);
+            if (j + 1 < ntiles) stash((j + 1) & 1);
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: one division by l, logsumexp, stores ----
@@ -997,16 +1083,29 @@ struct Tiling {
 // Tile shapes: 16-bit types (and FP8 scores) use fa_fwd_h_kernel (8 waves x
 // 32 query rows, 128-key tiles); fp32 uses fa_fwd_f32_kernel (4 waves x 32
 // query rows; 64-key tiles at d = 64, 32-key tiles at d = 128 for the LDS
-// budget).
+// budget).  At d = 64, an fp32 grid of fewer than kF32SplitBelow such
+// workgroups leaves most of the chip idle while each wave runs all of its
+// keys through its SIMD's fp32 matrix core in series; there the kernel runs
+// in its SPLIT form instead: 32-row workgroups of 8 waves that divide the
+// keys (32-key tiles) and merge their partial states.
 template <class T, int D>
 struct F32Choice {
     static constexpr int NQB = 1, NW = 4, NKB = (D == 64 ? 2 : 1);
     using C = Cfg<float, D, false, NQB, NW, NKB>;
 };
+constexpr int kF32SplitWaves = 8;
+constexpr long long kF32SplitBelow = 128;
+
+template <class T, int D>
+bool f32_split(int BH, int L) {
+    return sizeof(T) == 4 && D == 64 &&
+           (long long)BH * ((L + F32Choice<T, D>::C::BR - 1) / F32Choice<T, D>::C::BR) < kF32SplitBelow;
+}
 
 template <class T, int D, bool CAUSAL>
-Tiling tiling_of() {
+Tiling tiling_of(int BH, int L) {
     if constexpr (sizeof(T) == 2) return Tiling{HCfg<D>::BR, HCfg<D>::BC};
+    if (f32_split<T, D>(BH, L)) return Tiling{32, 32};
     using C = typename F32Choice<T, D>::C;
     return Tiling{C::BR, C::BC};
 }
@@ -1034,12 +1133,17 @@ inline Params make_params(const void* q, const void* k, const void* v, void* o, 
 template <class T, int D, bool CAUSAL>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int L, float scale,
            hipStream_t stream) {
-    const Tiling t = tiling_of<T, D, CAUSAL>();
+    const Tiling t = tiling_of<T, D, CAUSAL>(BH, L);
     const Params p = make_params(q, k, v, o, lse, BH, L, scale, t.br);
     const long long grid = (long long)BH * p.Tr;
     if constexpr (sizeof(T) == 2) {
         return fa_detail::launch_kernel(fa_fwd_h_kernel<T, D, CAUSAL, false>, dim3((unsigned)grid),
                                         dim3(HCfg<D>::NW * 64), stream, p);
+    } else if (f32_split<T, D>(BH, L)) {
+        if constexpr (D == 64)
+            return fa_detail::launch_kernel(fa_fwd_f32_kernel<float, D, CAUSAL, 1, kF32SplitWaves, 1, true>,
+                                            dim3((unsigned)grid), dim3(kF32SplitWaves * 64), stream, p);
+        return FA_ERR_UNSUPPORTED;
     } else {
         using Ch = F32Choice<T, D>;
         return fa_detail::launch_kernel(fa_fwd_f32_kernel<float, D, CAUSAL, Ch::NQB, Ch::NW, Ch::NKB>,
@@ -1048,15 +1152,17 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
 }
 
 template <class T>
-Tiling tiling_for(int d, int causal) {
-    if (d == 64) return causal ? tiling_of<T, 64, true>() : tiling_of<T, 64, false>();
-    return causal ? tiling_of<T, 128, true>() : tiling_of<T, 128, false>();
+Tiling tiling_for(int BH, int L, int d, int causal) {
+    if (d == 64) return causal ? tiling_of<T, 64, true>(BH, L) : tiling_of<T, 64, false>(BH, L);
+    return causal ? tiling_of<T, 128, true>(BH, L) : tiling_of<T, 128, false>(BH, L);
 }
 
-Tiling tiling_dispatch(int d, int causal, int dtype) {
-    if (dtype == FA_F32) return tiling_for<float>(d, causal);
-    if (dtype == FA_F16) return tiling_for<_Float16>(d, causal);
-    return tiling_for<__bf16>(d, causal);
+// BH = B*H: the fp32 shape depends on the grid size (callers have checked
+// that B*H fits an int)
+Tiling tiling_dispatch(int BH, int L, int d, int causal, int dtype) {
+    if (dtype == FA_F32) return tiling_for<float>(BH, L, d, causal);
+    if (dtype == FA_F16) return tiling_for<_Float16>(BH, L, d, causal);
+    return tiling_for<__bf16>(BH, L, d, causal);
 }
 
 int check_args(int B, int H, int L, int d, int causal, int dtype) {
@@ -1068,9 +1174,10 @@ int check_args(int B, int H, int L, int d, int causal, int dtype) {
     if (n >= (1LL << 62) / d) return FA_ERR_INVALID_ARG;
     // one head's tensor must stay below 2 GiB (32-bit buffer byte offsets)
     if ((long long)L * d * (dtype == FA_F32 ? 4 : 2) >= (1LL << 31)) return FA_ERR_INVALID_ARG;
-    const Tiling t = tiling_dispatch(d, causal, dtype);
+    if ((long long)B * H > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+    const Tiling t = tiling_dispatch(B * H, L, d, causal, dtype);
     const long long grid = (long long)B * H * ((L + t.br - 1) / t.br);
-    if (grid > 0x7fffffffLL || (long long)B * H > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+    if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
     return FA_OK;
 }
 
@@ -1167,7 +1274,7 @@ extern "C" int fa_fwd_tiling(int B, int H, int L, int d, int causal, int dtype, 
                              long long* workgroups) {
     const int rc = check_args(B, H, L, d, causal, dtype);
     if (rc != FA_OK) return rc;
-    const Tiling t = tiling_dispatch(d, causal, dtype);
+    const Tiling t = tiling_dispatch(B * H, L, d, causal, dtype);
     if (block_rows) *block_rows = t.br;
     if (block_cols) *block_cols = t.bc;
     if (workgroups) *workgroups = (long long)B * H * ((L + t.br - 1) / t.br);

@@ -94,6 +94,20 @@ def test_tiling_query():
         fa.fa_fwd_tiling(1, 1, 64, 80, 0, fa.FA_BF16)
 
 
+@pytest.mark.parametrize("BH,L,split", [(1, 256, True), (1, 1, True), (3, 1000, True), (31, 512, True),
+                                        (32, 512, False), (64, 300, False), (1, 16256, True), (1, 16257, False)])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_fp32_tiling_rule(BH, L, split, causal):
+    """fp32 at d = 64 divides the keys among a workgroup's waves (32-row, 32-key
+    tiles) exactly when the row-split grid (128-row tiles) has fewer than 128
+    workgroups; d = 128 and the 16-bit types keep their shapes."""
+    br, bc, wg = fa.fa_fwd_tiling(1, BH, L, 64, causal, fa.FA_F32)
+    assert (br, bc) == ((32, 32) if split else (128, 64))
+    assert wg == BH * ((L + br - 1) // br)
+    assert fa.fa_fwd_tiling(1, BH, L, 128, causal, fa.FA_F32)[:2] == (128, 32)
+    assert fa.fa_fwd_tiling(1, BH, L, 64, causal, fa.FA_BF16)[:2] == (256, 128)
+
+
 # ---- split-K/V entry points ---------------------------------------------------
 
 W = 1 << 24   # fake 256-byte-aligned workspace address

@@ -64,6 +64,27 @@ def test_edge_shapes(dtype, d, causal):
         compare(o, lse, o_ref, lse_ref, dtype, f"L={L} d={d} causal={causal}")
 
 
+# ---- fp32 at d = 64: keys divided among a workgroup's waves on small grids ----
+
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("BH,L", [(1, 256), (1, 31), (3, 1000), (1, 4097), (31, 512), (32, 512), (64, 300)])
+def test_fp32_split_and_row_forms(BH, L, causal):
+    """Both fp32 d = 64 forms against the oracle: the split-key form (fewer
+    than 128 row tiles; waves with no keys at L = 31, several tiles per wave at
+    L = 4097) and the row-split form (B*H = 32 and 64)."""
+    import io_aware_tiled_02_amd as fa
+    dtype, d = gen.F32, 64
+    br, _, _ = fa.fa_fwd_tiling(1, BH, L, d, causal, dtype)
+    say(f"[fp32] B=1 H={BH} L={L} causal={causal} block_rows={br}")
+    shape = (1, BH, L, d)
+    q = gen.fill(dtype, shape, 500 + L, 0, 1.5)
+    k = gen.fill(dtype, shape, 500 + L, 1, 1.5)
+    v = gen.fill(dtype, shape, 500 + L, 2)
+    o, lse = run_gpu(q, k, v, dtype, 0.125, causal)
+    o_ref, lse_ref = oracle.fwd(q, k, v, dtype, 0.125, causal)
+    compare(o, lse, o_ref, lse_ref, dtype, f"fp32 BH={BH} L={L} causal={causal}")
+
+
 @pytest.mark.parametrize("causal", [0, 1])
 def test_xcd_remap_many_heads(causal):
     """B*H a multiple of 8 (heads grouped per XCD) with a ragged last Q tile."""
