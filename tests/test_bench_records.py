@@ -24,9 +24,12 @@ def test_records_match_sources_or_are_ignored(wl):
         assert traffic is None
         return
     # measured HBM bytes of a call: at least the algorithmic bytes (within the
-    # counters' granularity), at most a few times them
+    # counters' granularity), at most a few times them.  The bound is 8x: a
+    # small grid spreads one head's workgroups over the 8 XCDs, and each XCD's
+    # L2 then fetches that head's K and V from memory itself (the fp32 L256
+    # workload: 8 workgroups, 5.05x).
     algo = entry["algorithmic_bytes_per_launch"]
-    assert 0.99 * algo <= traffic <= 5 * algo
+    assert 0.99 * algo <= traffic <= 8 * algo
     assert counters is not None and counters["hbm_gbps"] == pytest.approx(traffic / 1e-3 / 1e9)
     figures = [counters] + list(counters.get("kernels", {}).values())
     for f in figures:
