@@ -85,6 +85,22 @@ def traffic_for(workload):
 # transcendentals (v_exp_f32, v_log_f32, ...) run at a quarter of that rate.
 VALU_CYCLES, TRANS_CYCLES = 2.0, 8.0
 SIMDS, ENGINE_GHZ = 1024, 2.4
+# One wave's own issue rate, measured on gfx950 (one wave per SIMD issuing
+# independent v_fma_f32 / v_add_f32 / v_max3_f32, or v_exp_f32): a wave issues
+# a non-transcendental VALU instruction every 5.0 cycles and a transcendental
+# every 8.7.  The forward's softmax phases run one wave per SIMD at a time, so
+# at this rate, and at the engine clock measured under the counters, they
+# bound the kernel from below as well (the "one-wave issue bound").
+ONE_WAVE_VALU_CYCLES, ONE_WAVE_TRANS_CYCLES = 5.0, 8.7
+
+
+def one_wave_bound_ms(waves, valu, trans, clock_ghz):
+    """All waves' VALU work issued one wave per SIMD at a time at the one-wave
+    rates, in ms at `clock_ghz`; None without a clock figure."""
+    if not clock_ghz:
+        return None
+    cycles = (valu - trans) * ONE_WAVE_VALU_CYCLES + trans * ONE_WAVE_TRANS_CYCLES
+    return waves * cycles / (SIMDS * clock_ghz * 1e9) * 1e3
 
 
 def valu_roofline(workload, ms_per_launch):
@@ -100,6 +116,7 @@ def valu_roofline(workload, ms_per_launch):
     trans = pw["v_exp_f32"]
     cycles = (valu - trans) * VALU_CYCLES + trans * TRANS_CYCLES
     t_ms = w["waves"] * cycles / (SIMDS * ENGINE_GHZ * 1e9) * 1e3
+    t1 = one_wave_bound_ms(w["waves"], valu, trans, w.get("engine_clock_ghz"))
     return {
         "bound": "alu",
         "achieved": t_ms / ms_per_launch,
@@ -112,6 +129,11 @@ def valu_roofline(workload, ms_per_launch):
         "waves": w["waves"],
         "model": f"non-transcendental VALU {VALU_CYCLES:g} and transcendental {TRANS_CYCLES:g} SIMD cycles per "
                  f"wave64 instruction, {SIMDS} SIMDs at {ENGINE_GHZ} GHz",
+        "one_wave_bound_ms": t1,
+        "one_wave_frac": None if t1 is None else t1 / ms_per_launch,
+        "one_wave_model": f"the same VALU work issued one wave per SIMD at a time, {ONE_WAVE_VALU_CYCLES:g} / "
+                          f"{ONE_WAVE_TRANS_CYCLES:g} cycles per instruction (measured one-wave rates), at the engine "
+                          "clock measured under the counters",
     }
 
 
@@ -956,6 +978,12 @@ def summarize_counters(args):
         md += [f"  - VALU issue bound of `{k}` ({nv:.0f} VALU instructions per wave besides MFMA, {nt:.0f} of them "
                f"transcendental; {VALU_CYCLES:g} / {TRANS_CYCLES:g} SIMD cycles per wave64 instruction, {SIMDS} SIMDs at "
                f"{ENGINE_GHZ} GHz): {tv:.4f} ms, {tv / d_['duration_ms_under_counters']:.3f} of the duration under counters"]
+        t1 = one_wave_bound_ms(d_["waves"], nv, nt, d_["engine_clock_ghz"])
+        if t1 is not None:
+            md += [f"  - One-wave issue bound (the same work issued one wave per SIMD at a time, "
+                   f"{ONE_WAVE_VALU_CYCLES:g} / {ONE_WAVE_TRANS_CYCLES:g} cycles per instruction, at "
+                   f"{d_['engine_clock_ghz']:.2f} GHz): {t1:.4f} ms, {t1 / d_['duration_ms_under_counters']:.3f} of the "
+                   "duration under counters"]
     open(os.path.join(pdir, f"{prefix}_{tag}_sq_counters.md"), "w").write("\n".join(md) + "\n")
 
     md = [f"# {prefix}, {title} — HBM traffic\n", head, "```", *cmds["traffic"], "```\n",
