@@ -978,7 +978,9 @@ def summarize_counters(args):
         md += [f"  - VALU issue bound of `{k}` ({nv:.0f} VALU instructions per wave besides MFMA, {nt:.0f} of them "
                f"transcendental; {VALU_CYCLES:g} / {TRANS_CYCLES:g} SIMD cycles per wave64 instruction, {SIMDS} SIMDs at "
                f"{ENGINE_GHZ} GHz): {tv:.4f} ms, {tv / d_['duration_ms_under_counters']:.3f} of the duration under counters"]
-        t1 = one_wave_bound_ms(d_["waves"], nv, nt, d_["engine_clock_ghz"])
+        # the forward's softmax phases run one wave per SIMD at a time; the
+        # other kernels' waves run free, so this bound is the forward's alone
+        t1 = one_wave_bound_ms(d_["waves"], nv, nt, d_["engine_clock_ghz"]) if spec["family"] == "fwd" else None
         if t1 is not None:
             md += [f"  - One-wave issue bound (the same work issued one wave per SIMD at a time, "
                    f"{ONE_WAVE_VALU_CYCLES:g} / {ONE_WAVE_TRANS_CYCLES:g} cycles per instruction, at "

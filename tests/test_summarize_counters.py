@@ -127,6 +127,9 @@ def test_summarize_counters_on_synthetic_output(tmp_path, wl):
     # both VALU bounds, the second at the planted clock
     sq_md = (out / f"{spec['prefix']}_{spec['tag']}_sq_counters.md").read_text()
     assert sq_md.count("VALU issue bound of") == nk
-    assert sq_md.count(f"One-wave issue bound") == nk and f"at {CLOCK_GHZ:.2f} GHz" in sq_md
+    if spec["family"] == "fwd":
+        assert sq_md.count("One-wave issue bound") == nk and f"at {CLOCK_GHZ:.2f} GHz" in sq_md
+    else:
+        assert "One-wave issue bound" not in sq_md
     rec = json.load(open(out / os.path.basename(bench._record_path("traffic", spec["family"]))))
     assert rec["workloads"][wl]["algorithmic_bytes_per_launch"] == spec["algo"]
