@@ -356,11 +356,14 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                T o4[4];
+            for (int gp = 0; gp < 2; ++gp) {
+                T a4[4], b4[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o4[e] = (T)(acc[dt][4 * g + e] * p.scale);
-                st8(qrow + (dt * 32 + g * 8 + hf * 4) * 2, __builtin_bit_cast(u32x2, o4));
+                for (int e = 0; e < 4; ++e) {
+                    a4[e] = (T)(acc[dt][8 * gp + e] * p.scale);
+                    b4[e] = (T)(acc[dt][8 * gp + 4 + e] * p.scale);
+                }
+                store_chunk_pair<T>(qrow, 4 * dt + 2 * gp, hf, a4, b4);
             }
     }
 }
@@ -553,15 +556,17 @@ __device__ __attribute__((always_inline)) inline void fa_bwd_dkdv_body(const Bwd
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                T k4[4], v4[4];
+            for (int gp = 0; gp < 2; ++gp) {
+                T ka[4], kb4[4], va[4], vb[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    k4[e] = (T)(dka[dt][4 * g + e] * p.scale);
-                    v4[e] = (T)dva[dt][4 * g + e];
+                    ka[e] = (T)(dka[dt][8 * gp + e] * p.scale);
+                    kb4[e] = (T)(dka[dt][8 * gp + 4 + e] * p.scale);
+                    va[e] = (T)dva[dt][8 * gp + e];
+                    vb[e] = (T)dva[dt][8 * gp + 4 + e];
                 }
-                st8(krow + (dt * 32 + g * 8 + hf * 4) * 2, __builtin_bit_cast(u32x2, k4));
-                st8(vrow + (dt * 32 + g * 8 + hf * 4) * 2, __builtin_bit_cast(u32x2, v4));
+                store_chunk_pair<T>(krow, 4 * dt + 2 * gp, hf, ka, kb4);
+                store_chunk_pair<T>(vrow, 4 * dt + 2 * gp, hf, va, vb);
             }
     }
 }

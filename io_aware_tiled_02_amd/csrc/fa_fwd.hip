@@ -1063,11 +1063,14 @@ void fa_fwd_h_kernel(Params p) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                T o4[4];
+            for (int gp = 0; gp < 2; ++gp) {
+                T a4[4], b4[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[dt][4 * g + e] * inv);
-                st8(orow + (dt * 32 + g * 8 + hf * 4) * 2, __builtin_bit_cast(u32x2, o4));
+                for (int e = 0; e < 4; ++e) {
+                    a4[e] = (T)(oacc[dt][8 * gp + e] * inv);
+                    b4[e] = (T)(oacc[dt][8 * gp + 4 + e] * inv);
+                }
+                store_chunk_pair<T>(orow, 4 * dt + 2 * gp, hf, a4, b4);
             }
         if (hf == 0) p.lse[(long long)bh * L + query] = (mc + __builtin_amdgcn_logf(ltot)) * kLn2;
     }
