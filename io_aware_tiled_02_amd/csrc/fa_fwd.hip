@@ -1043,16 +1043,18 @@ void fa_fwd_h_kernel(Params p) {
             end_x();
         }
         mma_run(yes{}, no{}, j, PR{});                  // j == ntw: last PV
-        end_m();
+        if (j < ntiles || group == 0) end_m();
         if (j < ntiles) end_x();
         ++j;
     }
     for (; j <= ntiles; ++j) {                    // phases of tiles this wave does not need
         if (feeder && j < ntiles) dma_tile(j);
-        end_m();
+        if (j < ntiles || group == 0) end_m();
         if (j < ntiles) end_x();
     }
-    if (group == 0) __syncthreads();              // group 0 ends one phase later
+    // The last phase (group 1's final P V) needs no barrier after it: group 0
+    // goes on to its epilogue, which touches no LDS, while group 1 finishes;
+    // each wave has now passed the same number of barriers.
 
     // epilogue: one division by l, logsumexp, stores
     const float ltot = pair_sum(lsum);
