@@ -10,8 +10,11 @@
 // A block is `block` consecutive rows of one (batch, head), all d columns:
 // one contiguous span of the (B, H, L, d) tensor.  One workgroup per block
 // loads it into registers, reduces the maximum and converts what it holds,
-// so the kernel moves 2 + 1 bytes of HBM per element (blocks beyond 16K
-// elements are read a second time instead of held).  The arithmetic is float32:
+// so the kernel moves 2 + 1 bytes of HBM per element.  Blocks beyond 16K
+// elements take a second kernel that reads the block twice instead of holding
+// it; keeping the two apart leaves the common kernel free of a branch on the
+// block size, which lets all of its loads issue before the first wait.  The
+// arithmetic is float32:
 // s = amax / 448 and x / s are IEEE-rounded divisions, and the quotient is
 // clamped to +-448 before conversion (the conversion does not saturate; the
 // clamp only absorbs the rounding of s).
@@ -58,31 +61,27 @@ __device__ inline float piece_amax(const u32x4 raw) {
     return m;
 }
 
+// Blocks of at most 256 * kKeep pieces: held in registers, HBM read once.
 template <class T>
-__global__ __launch_bounds__(256) void fa_quant_kernel(const char* x, unsigned char* x8, float* scales, int L,
-                                                       int d, int block, int nblk) {
+__global__ __launch_bounds__(256) void fa_quant_kept_kernel(const char* x, unsigned char* x8, float* scales, int L,
+                                                            int d, int block, int nblk) {
     const int b = blockIdx.x, bh = blockIdx.y;
     const int r0 = b * block, r1 = min(r0 + block, L);
     const long long e0 = ((long long)bh * L + r0) * d;
-    const long long n8 = (long long)(r1 - r0) * d / 8;   // 16-byte input pieces of the block
+    const int n8 = (r1 - r0) * d / 8;                     // <= 256 * kKeep, checked by the host
     const char* src = x + e0 * 2;
     unsigned char* dst = x8 + e0;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool keep = n8 <= 256 * kKeep;
 
     u32x4 held[kKeep];
-    float amax = 0.f;
-    if (keep) {
 #pragma unroll
-        for (int p = 0; p < kKeep; ++p) {
-            const int i = tid + 256 * p;
-            held[p] = i < n8 ? ld16(src + (long long)i * 16) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int p = 0; p < kKeep; ++p) amax = fmaxf(amax, piece_amax<T>(held[p]));
-    } else {
-        for (long long i = tid; i < n8; i += 256) amax = fmaxf(amax, piece_amax<T>(ld16(src + i * 16)));
+    for (int p = 0; p < kKeep; ++p) {
+        const int i = tid + 256 * p;
+        held[p] = i < n8 ? ld16(src + (long long)i * 16) : u32x4{0, 0, 0, 0};
     }
+    float amax = 0.f;
+#pragma unroll
+    for (int p = 0; p < kKeep; ++p) amax = fmaxf(amax, piece_amax<T>(held[p]));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     __shared__ float red[4];
@@ -91,16 +90,45 @@ __global__ __launch_bounds__(256) void fa_quant_kernel(const char* x, unsigned c
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float s = amax > 0.f ? amax / kE4M3Max : 1.f;
     if (tid == 0) scales[(long long)bh * nblk + b] = s;
-
-    if (keep) {
 #pragma unroll
-        for (int p = 0; p < kKeep; ++p) {
-            const int i = tid + 256 * p;
-            if (i < n8) quant_store<T>(held[p], s, dst + (long long)i * 8);
-        }
-    } else {
-        for (long long i = tid; i < n8; i += 256) quant_store<T>(ld16(src + i * 16), s, dst + i * 8);
+    for (int p = 0; p < kKeep; ++p) {
+        const int i = tid + 256 * p;
+        if (i < n8) quant_store<T>(held[p], s, dst + (long long)i * 8);
     }
+}
+
+// Larger blocks: one pass for the maximum, a second that reads and converts.
+template <class T>
+__global__ __launch_bounds__(256) void fa_quant_streamed_kernel(const char* x, unsigned char* x8, float* scales,
+                                                                int L, int d, int block, int nblk) {
+    const int b = blockIdx.x, bh = blockIdx.y;
+    const int r0 = b * block, r1 = min(r0 + block, L);
+    const long long e0 = ((long long)bh * L + r0) * d;
+    const long long n8 = (long long)(r1 - r0) * d / 8;   // 16-byte input pieces of the block
+    const char* src = x + e0 * 2;
+    unsigned char* dst = x8 + e0;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    float amax = 0.f;
+    for (long long i = tid; i < n8; i += 256) amax = fmaxf(amax, piece_amax<T>(ld16(src + i * 16)));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    __shared__ float red[4];
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax > 0.f ? amax / kE4M3Max : 1.f;
+    if (tid == 0) scales[(long long)bh * nblk + b] = s;
+    for (long long i = tid; i < n8; i += 256) quant_store<T>(ld16(src + i * 16), s, dst + i * 8);
+}
+
+template <class T>
+int launch_quant(const void* x, void* x8, float* scales, int L, int d, int block, int nblk, dim3 grid,
+                 hipStream_t stream) {
+    const bool kept = (long long)block * d / 8 <= 256 * kKeep;
+    return fa_detail::launch_kernel(kept ? fa_quant_kept_kernel<T> : fa_quant_streamed_kernel<T>, grid, dim3(256),
+                                    stream, static_cast<const char*>(x), static_cast<unsigned char*>(x8), scales, L,
+                                    d, block, nblk);
 }
 
 }  // namespace
@@ -117,9 +145,6 @@ extern "C" int fa_quantize_fp8(const void* x, int dtype, int B, int H, int L, in
     if (((uintptr_t)x | (uintptr_t)x8) % 16 != 0 || (uintptr_t)scales % 4 != 0) return FA_ERR_ALIGN;
     const long long nblk = ((long long)L + block - 1) / block;     // <= L
     const dim3 grid((unsigned)nblk, (unsigned)(B * H));
-    if (dtype == FA_BF16)
-        return fa_detail::launch_kernel(fa_quant_kernel<__bf16>, grid, dim3(256), stream, static_cast<const char*>(x),
-                                        static_cast<unsigned char*>(x8), scales, L, d, block, (int)nblk);
-    return fa_detail::launch_kernel(fa_quant_kernel<_Float16>, grid, dim3(256), stream, static_cast<const char*>(x),
-                                    static_cast<unsigned char*>(x8), scales, L, d, block, (int)nblk);
+    if (dtype == FA_BF16) return launch_quant<__bf16>(x, x8, scales, L, d, block, (int)nblk, grid, stream);
+    return launch_quant<_Float16>(x, x8, scales, L, d, block, (int)nblk, grid, stream);
 }

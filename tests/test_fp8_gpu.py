@@ -97,7 +97,7 @@ def compare_fp8(o, lse, o_ref, lse_ref, tol_lse, label):
 @pytest.mark.parametrize("d", [64, 128])
 def test_quantize_bit_exact(dtype, d):
     for (L, block, sigma) in [(1, 1, 1.0), (37, 16, 2.0), (128, 128, 1.0), (300, 64, 30.0), (300, 1000, 0.01),
-                              (129, 7, 1.0), (520, 128, 3.0)]:
+                              (129, 7, 1.0), (520, 128, 3.0), (2150, 300, 1.0)]:
         say(f"[quant] dtype={gen.DTYPE_NAMES[dtype]} d={d} L={L} block={block} sigma={sigma}")
         x = gen.fill(dtype, (2, 3, L, d), 500 + L, 0, sigma)
         if L >= 2 * block:
