@@ -27,6 +27,9 @@
 //    lane holds are exactly the B operand it needs, so P never leaves
 //    registers.
 //  * 16-bit types (fa_fwd_h_kernel): 8 waves, 256 query rows, 128-key tiles.
+//    With fp16 P, m there is a reference that may trail the running maximum
+//    by a bounded amount, so O and l are rescaled only when some row's
+//    maximum has moved well past it (the reference cancels in O / l and lse).
 //    K and V tiles are double-buffered in LDS and filled by LDS-DMA
 //    (buffer_load ... lds, no register staging); V^T operands come from
 //    row-major V through ds_read_b64_tr_b16.  The two groups of 4 waves run
@@ -610,6 +613,20 @@ struct SliceOrder {
     }
 };
 
+// How far (in base-2 units of scaled scores) the reference a row's P is taken
+// against may trail the row's running maximum.  The reference cancels in O / l
+// and in lse = ref + log l, so in exact arithmetic any value gives the same
+// result, and a trail of at most 8 keeps P <= 256, far inside the 16-bit
+// range, while sparing the rescale of O in most tiles once the maxima have
+// settled.  In rounded arithmetic it costs the exactness of the dominant
+// weight: with the reference at the maximum that weight is exactly 1, with a
+// trailing one it is 2^delta rounded to the P type, a relative error of up to
+// half an ulp of that type which shows in rows one key dominates.  fp16 P
+// (11 significant bits) keeps that near the rounding of O itself; bf16 P (8)
+// would not, so bf16 keeps the reference at the maximum.
+template <class T>
+constexpr float ref_lag() { return std::is_same<T, _Float16>::value ? 8.f : 0.f; }
+
 // Ping-pong schedule.  The 8 waves form two groups of 4 (waves 0-3 and 4-7);
 // each SIMD runs one wave of each group.  Per K/V tile j a wave has
 //     M(j): O^T += V_{j-1}^T P_{j-1}^T  and  S_j = K_j Q^T        (MFMA)
@@ -949,20 +966,34 @@ void fa_fwd_h_kernel(Params p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
         }
-        // running max mc in scaled log2 units (-inf while no key is seen);
-        // O and l are rescaled only in waves where some row's max moved
+        // reference mc in scaled log2 units (-inf while no key is seen).  It
+        // trails the running max by at most ref_lag<T>(): O and l are
+        // rescaled, and every row's mc brought up to its max, only in tiles
+        // where some row of the wave passed its mc by more than that
         const float cand = FP8 ? pair_max(mx) : pair_max(mx) * p.c;
-        const bool bump = cand > mc;
-        const float alpha = bump ? __builtin_amdgcn_exp2f(mc - cand) : 1.f;
-        mc = bump ? cand : mc;
-        const float ref = (mc == -INFINITY) ? 0.f : mc;
-        lsum *= alpha;
-        if (__ballot(bump)) {
+        constexpr float lag = ref_lag<T>();
+        auto rescale = [&](float alpha) {
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        };
+        if constexpr (lag > 0.f) {
+            if (__ballot(cand > mc + lag)) {
+                const bool bump = cand > mc;
+                const float alpha = bump ? __builtin_amdgcn_exp2f(mc - cand) : 1.f;
+                mc = bump ? cand : mc;
+                lsum *= alpha;
+                rescale(alpha);
+            }
+        } else {
+            const bool bump = cand > mc;
+            const float alpha = bump ? __builtin_amdgcn_exp2f(mc - cand) : 1.f;
+            mc = bump ? cand : mc;
+            lsum *= alpha;
+            if (__ballot(bump)) rescale(alpha);
         }
+        const float ref = (mc == -INFINITY) ? 0.f : mc;
 #pragma unroll
         for (int kt = 0; kt < NKB; ++kt)
 #pragma unroll

@@ -157,6 +157,27 @@ def test_dominant_score_selects_value_row():
     assert np.max(np.abs(o[0, 0, sel] - vstar)) <= 1e-2
 
 
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.F16])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_rising_row_maxima(dtype, causal):
+    """Row maxima that climb from tile to tile at rates from far below to far
+    above what the kernel lets its softmax reference trail by (8 base-2 units),
+    a late jump, and rows whose maximum lies in the first tile: every pattern
+    of skipped and taken rescales, checked on every row."""
+    B, H, L, d = 1, 2, 1000, 64
+    say(f"[closed] rising maxima dtype={gen.DTYPE_NAMES[dtype]} causal={causal}")
+    q = gen.to_float64(gen.fill(dtype, (B, H, L, d), 12, 0, 0.3), dtype)
+    k = gen.to_float64(gen.fill(dtype, (B, H, L, d), 12, 1, 0.3), dtype)
+    q[..., 0] = np.linspace(-8.0, 8.0, L)          # row i's score slope along the keys
+    k[..., 0] = 64.0 * np.arange(L) / L             # keys rise: up to 12 base-2 units per 128-key tile
+    k[:, 1, 900, 0] = 96.0                          # and one late jump in head 1
+    q, k = gen.from_float64(q, dtype), gen.from_float64(k, dtype)
+    v = gen.fill(dtype, (B, H, L, d), 12, 2)
+    o, lse = run_gpu(q, k, v, dtype, 0.125, causal)
+    o_ref, lse_ref = oracle.fwd(q, k, v, dtype, 0.125, causal)
+    compare(o, lse, o_ref, lse_ref, dtype, f"rising maxima causal={causal}")
+
+
 @pytest.mark.parametrize("dtype", [gen.BF16, gen.F16, gen.F32])
 def test_causal_first_row_is_first_value_row(dtype):
     B, H, L, d = 1, 2, 333, 128
