@@ -22,7 +22,9 @@
 //  * The score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_{bf16,f16}: in the 32x32 accumulator layout a lane
 //    holds ONE query (its column) and 16 keys, so the row max and row sum are
-//    plain in-register max/add chains plus one exchange with lane^32.
+//    plain in-register max/add chains plus one exchange with lane^32.  (fp16
+//    at d = 64 forms the row sum on the matrix core instead, from the rounded
+//    P that multiplies V.)
 //  * The output is accumulated transposed too, O^T += V^T P^T: the P values a
 //    lane holds are exactly the B operand it needs, so P never leaves
 //    registers.
@@ -568,6 +570,23 @@ struct K8Layout {
 };
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Row sums of P on the matrix core.  v_mfma_f32_16x16x32_f16 reads a lane's P
+// fragment (the 32x32x16 B operand: query l % 32, 8 keys) as column l % 16 of
+// k-group l / 16, so query q's fragments sit in k-groups 0 and 2 of column q
+// (q < 16) or in k-groups 1 and 3 of column q - 16.  This A operand has ones
+// in row 0 over k-groups 0 and 2 (lanes 0, 32) and in row 4 over k-groups 1
+// and 3 (lanes 20, 52), zeros elsewhere; the product then holds query q's sum
+// in row 0 or 4 of column q % 16, which the 16x16 result layout puts in
+// register 0 of lane q.  Lanes 32-63 hold zeros.
+__device__ inline f16x8 row_sum_selector(int lane) {
+    const bool one = lane == 0 || lane == 32 || lane == 20 || lane == 52;
+    f16x8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = one ? (_Float16)1.f : (_Float16)0.f;
+    return a;
+}
 
 // S^T += K Q^T over 64 d-values with E4M3 codes: the K row chunks (a0, a1)
 // and Q row chunks (b0, b1) hold 32 consecutive d-values of the lane's
@@ -770,6 +789,13 @@ void fa_fwd_h_kernel(Params p) {
     }
 
     float mc = -INFINITY, lsum = 0.f;
+    // fp16 at d = 64, where the softmax's VALU work bounds the kernel and the
+    // matrix core has room: l is the row sum of the rounded P (the weights
+    // P V uses), accumulated on the matrix core beside P V in lacc, instead
+    // of 64 VALU adds per lane and tile into lsum
+    constexpr bool LMMA = std::is_same<T, _Float16>::value && D == 64;
+    f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+    const f16x8 lsel = row_sum_selector(lane);
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -872,6 +898,9 @@ void fa_fwd_h_kernel(Params p) {
             if (i < NPV) {
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = Ty<T>::mma(buf[pos & 1][dt], pf[i >> 1][i & 1], oacc[dt]);
+                if constexpr (LMMA)
+                    lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lsel, __builtin_bit_cast(f16x8, pf[i >> 1][i & 1]),
+                                                                 lacc, 0, 0, 0);
             } else if constexpr (FP8) {
                 const int kt = i - NPV;
 #pragma unroll
@@ -905,6 +934,7 @@ void fa_fwd_h_kernel(Params p) {
                     if (rd == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then LDS reads
                     else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
+                if (LMMA && ord.v[i] < NPV) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the row sums
             } else if (more) {
                 // FP8 score slices hold D/64 (longer) MFMAs and D/32 reads;
                 // PV slices D/32 MFMAs with two reads each
@@ -985,13 +1015,17 @@ void fa_fwd_h_kernel(Params p) {
                 mc = bump ? cand : mc;
                 lsum *= alpha;
                 rescale(alpha);
+                if constexpr (LMMA) lacc[0] *= alpha;
             }
         } else {
             const bool bump = cand > mc;
             const float alpha = bump ? __builtin_amdgcn_exp2f(mc - cand) : 1.f;
             mc = bump ? cand : mc;
             lsum *= alpha;
-            if (__ballot(bump)) rescale(alpha);
+            if (__ballot(bump)) {
+                rescale(alpha);
+                if constexpr (LMMA) lacc[0] *= alpha;
+            }
         }
         const float ref = (mc == -INFINITY) ? 0.f : mc;
 #pragma unroll
@@ -1002,7 +1036,7 @@ void fa_fwd_h_kernel(Params p) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * ps + e], FP8 ? ck[kt] : p.c, -ref));
-                    lsum += pe[e];
+                    if constexpr (!LMMA) lsum += pe[e];
                 }
                 pf[kt][ps] = Ty<T>::cvt(pe);
             }
@@ -1088,7 +1122,7 @@ void fa_fwd_h_kernel(Params p) {
     // each wave has now passed the same number of barriers.
 
     // epilogue: one division by l, logsumexp, stores
-    const float ltot = pair_sum(lsum);
+    const float ltot = pair_sum(LMMA ? lacc[0] : lsum);
     const float inv = 1.f / ltot;
     const int query = qw + l32;
     if (query < L) {
