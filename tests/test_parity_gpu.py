@@ -210,6 +210,44 @@ def test_causal_first_row_is_first_value_row(dtype):
     np.testing.assert_allclose(lse[:, :, 0], qk, atol=1e-4)
 
 
+# ---- seeded random shapes -------------------------------------------------------
+
+def _random_cases(n, seed):
+    """(B, H, L, d, dtype, causal, sigma) drawn from the input generator's
+    SplitMix64 integers (stream 8), so the cases are fixed by the seed."""
+    draws = gen.splitmix64(seed, 8, 0, 7 * n)
+    cases = []
+    for i in range(n):
+        u = [int(x) for x in draws[7 * i:7 * i + 7]]
+        B = 1 + u[0] % 2
+        H = 1 + u[1] % 5
+        L = 1 + u[2] % 2500
+        d = (64, 128)[u[3] % 2]
+        dtype = (gen.BF16, gen.F16)[u[4] % 2]
+        causal = u[5] % 2
+        sigma = (0.5, 1.0, 2.0, 3.0)[u[6] % 4]
+        cases.append((B, H, L, d, dtype, causal, sigma))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(24, 2024))
+def test_random_shapes(case):
+    """Seeded random (B, H, L, d, type, mask, spread): ragged tails at any
+    length, several tiles, both head sizes and both 16-bit types (so both
+    softmax forms), every row against the oracle."""
+    B, H, L, d, dtype, causal, sigma = case
+    say(f"[random] B={B} H={H} L={L} d={d} dtype={gen.DTYPE_NAMES[dtype]} causal={causal} sigma={sigma}")
+    shape = (B, H, L, d)
+    seed = 3000 + L
+    q = gen.fill(dtype, shape, seed, 0, sigma)
+    k = gen.fill(dtype, shape, seed, 1, sigma)
+    v = gen.fill(dtype, shape, seed, 2)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_gpu(q, k, v, dtype, scale, causal)
+    o_ref, lse_ref = oracle.fwd(q, k, v, dtype, scale, causal)
+    compare(o, lse, o_ref, lse_ref, dtype, f"random {case}")
+
+
 # ---- determinism and no stale tiles ---------------------------------------------
 
 def test_repeat_launch_is_bitwise_identical():
