@@ -138,16 +138,16 @@ __device__ inline void dma16(i32x4 rsrc, int voff, unsigned lds_base) {
 // chunks (c0, c0 + 1) lets the lower lane store chunk c0 and the upper lane
 // chunk c0 + 1 as one 16-byte store each, instead of two 8-byte stores per
 // lane.  `lo` and `hi` are this lane's halves of chunks c0 and c0 + 1; both
-// lanes of the pair must call it (they share the row).
+// lanes of the pair must call it (they share the row).  The exchange is
+// v_permlane32_swap of (lo, hi): it trades the upper lanes' lo with the lower
+// lanes' hi, which leaves the lower lane holding both halves of chunk c0 and
+// the upper lane both halves of chunk c0 + 1, each in order.
 template <class T>
 __device__ inline void store_chunk_pair(char* row, int c0, int h, const T (&lo)[4], const T (&hi)[4]) {
     const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
-    const u32x2 x = h ? a : b;                        // the half the other lane stores
-    u32x2 r;
-    r[0] = (unsigned)__shfl_xor((int)x[0], 32);
-    r[1] = (unsigned)__shfl_xor((int)x[1], 32);
-    const u32x4 out = h ? u32x4{r[0], r[1], b[0], b[1]} : u32x4{a[0], a[1], r[0], r[1]};
-    st16(row + (c0 + h) * 8 * (int)sizeof(T), out);
+    const auto s0 = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+    st16(row + (c0 + h) * 8 * (int)sizeof(T), u32x4{s0[0], s1[0], s0[1], s1[1]});
 }
 
 // Exchange with lane^32 (v_permlane32_swap): returns the pair {x, x of lane^32}.

@@ -650,6 +650,7 @@ constexpr float ref_lag() { return std::is_same<T, _Float16>::value ? 8.f : 0.f;
 // each SIMD runs one wave of each group.  Per K/V tile j a wave has
 //     M(j): O^T += V_{j-1}^T P_{j-1}^T  and  S_j = K_j Q^T        (MFMA)
 //     X(j): row max, rescale, P_j = exp2(scale*S_j - ref), l     (VALU)
+// (fp16 at d = 64 adds P_{j-1}'s row sums to l in M(j), on the matrix core)
 // and the groups run them in alternate phases fenced by workgroup barriers:
 //     phase   0    1    2    3   ...  2T   2T+1
 //     group 0 M(0) X(0) M(1) X(1) ... M(T)  -
