@@ -38,9 +38,9 @@ constexpr float kE4M3Max = 448.f;
 // once; larger blocks read it twice.
 constexpr int kKeep = 8;
 
-// x is read once and x8 written once: both carry the nontemporal hint, so the
-// stream does not displace cached lines (21 -> 19 us per 64 MiB bf16 tensor,
-// results bitwise equal)
+// x is read once (its last read, in the two-pass kernel) and x8 written once:
+// those accesses carry the nontemporal hint, so the stream does not displace
+// cached lines (21 -> 19 us per 64 MiB bf16 tensor, results bitwise equal)
 __device__ inline u32x4 ld16_streamed(const char* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -117,7 +117,8 @@ __global__ __launch_bounds__(256) void fa_quant_streamed_kernel(const char* x, u
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     float amax = 0.f;
-    for (long long i = tid; i < n8; i += 256) amax = fmaxf(amax, piece_amax<T>(ld16_streamed(src + i * 16)));
+    // the first pass leaves the block in the caches for the second
+    for (long long i = tid; i < n8; i += 256) amax = fmaxf(amax, piece_amax<T>(ld16(src + i * 16)));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     __shared__ float red[4];
