@@ -111,8 +111,8 @@ int fa_fwd_tiling(int B, int H, int L, int d, int causal, int dtype,
 
 /*
  * fa_splitkv_splits -- the nsplit that fa_fwd_splitkv uses when passed
- * nsplit <= 0: enough chunks to occupy the GPU, at least 256 keys each.
- * Returns 0 for non-positive sizes.
+ * nsplit <= 0: chunks for about 2048 wavefronts in all (a multiple of 4 when
+ * above 4), at least 256 keys each.  Returns 0 for non-positive sizes.
  */
 int fa_splitkv_splits(int B, int H, int Lk);
 

@@ -190,7 +190,10 @@ def test_splitkv_workspace_size_and_auto_splits():
     assert _sk(wsz=4 * 8 * 128 * 4 + 255) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_splitkv_workspace_bytes(0, 4, 1, 1000, 128, 4) == 0
     s = fa.fa_splitkv_splits(1, 32, 32768)
-    assert 1 <= s <= (32768 + 255) // 256 and 32 * s >= 2048
+    assert 1 <= s <= (32768 + 255) // 256 and 32 * s >= 2048 and s % 4 == 0
+    assert fa.fa_splitkv_splits(8, 32, 16384) == 8              # about 2048 waves in all
+    assert fa.fa_splitkv_splits(4, 25, 16384) == 24             # 21 rounded up to whole workgroups
+    assert fa.fa_splitkv_splits(16, 32, 8192) == 4
     assert fa.fa_splitkv_splits(1, 1, 100) == 1                 # at least 256 keys per chunk
     assert fa.fa_splitkv_workspace_bytes(1, 32, 1, 32768, 128, 0) == \
         fa.fa_splitkv_workspace_bytes(1, 32, 1, 32768, 128, s)
