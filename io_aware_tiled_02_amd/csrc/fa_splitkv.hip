@@ -240,7 +240,7 @@ int elem_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
 // 256 keys each.  Above 4 the count is a multiple of 4, so every workgroup's
 // four waves have a chunk.  Measured on decoding shapes (Lq 1 to 4, B*H 32 to
 // 512, Lk 8K to 64K): fewer, longer streams read HBM faster than the 4096
-// shorter ones this rule replaced, by up to 23%; at Lq <= 2 about 1024 waves
+// shorter ones this rule replaced, by up to 12%; at Lq <= 2 about 1024 waves
 // read faster still, at Lq = 4 they fall behind.
 int auto_splits(int B, int H, int Lk) {
     const long long bh = (long long)B * H;
