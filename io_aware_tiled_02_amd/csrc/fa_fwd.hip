@@ -632,6 +632,26 @@ struct SliceOrder {
     }
 };
 
+// Whether any of the lane's fp16 P values (all >= 0, or +inf where a value
+// overflowed) exceeds lim: a packed maximum over the P registers,
+// v_pk_maximum3_f16 taking two registers (four values) per instruction.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <class F, int N>
+__device__ inline bool p16_above(const F (&pf)[N][2], _Float16 lim) {
+    f16x2 m = {(_Float16)0.f, (_Float16)0.f};
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f16x8 v = __builtin_bit_cast(f16x8, pf[i][h]);
+            m = __builtin_elementwise_maximum(m, __builtin_shufflevector(v, v, 0, 1));
+            m = __builtin_elementwise_maximum(m, __builtin_shufflevector(v, v, 2, 3));
+            m = __builtin_elementwise_maximum(m, __builtin_shufflevector(v, v, 4, 5));
+            m = __builtin_elementwise_maximum(m, __builtin_shufflevector(v, v, 6, 7));
+        }
+    return __builtin_elementwise_maximum(m[0], m[1]) > lim;
+}
+
 // How far (in base-2 units of scaled scores) the reference a row's P is taken
 // against may trail the row's running maximum.  The reference cancels in O / l
 // and in lse = ref + log l, so in exact arithmetic any value gives the same
@@ -980,28 +1000,27 @@ void fa_fwd_h_kernel(Params p) {
 #pragma unroll
             for (int kt = 0; kt < NKB; ++kt) ck[kt] = cq * ks[kt];
         }
-        float mx;
-        if constexpr (FP8) {
-            mx = -INFINITY;
+        // the exact row maximum of the tile's scores, in scaled log2 units
+        auto row_max = [&]() -> float {
+            float mx;
+            if constexpr (FP8) {
+                mx = -INFINITY;
 #pragma unroll
-            for (int kt = 0; kt < NKB; ++kt) {
-                float m = sacc[kt][0];
+                for (int kt = 0; kt < NKB; ++kt) {
+                    float m = sacc[kt][0];
 #pragma unroll
-                for (int r = 1; r < 16; ++r) m = fmaxf(m, sacc[kt][r]);
-                mx = fmaxf(mx, m * ck[kt]);
+                    for (int r = 1; r < 16; ++r) m = fmaxf(m, sacc[kt][r]);
+                    mx = fmaxf(mx, m * ck[kt]);
+                }
+            } else {
+                mx = sacc[0][0];
+#pragma unroll
+                for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
             }
-        } else {
-            mx = sacc[0][0];
-#pragma unroll
-            for (int kt = 0; kt < NKB; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-        }
-        // reference mc in scaled log2 units (-inf while no key is seen).  It
-        // trails the running max by at most ref_lag<T>(): O and l are
-        // rescaled, and every row's mc brought up to its max, only in tiles
-        // where some row of the wave passed its mc by more than that
-        const float cand = FP8 ? pair_max(mx) : pair_max(mx) * p.c;
+            return FP8 ? pair_max(mx) : pair_max(mx) * p.c;
+        };
         constexpr float lag = ref_lag<T>();
         auto rescale = [&](float alpha) {
 #pragma unroll
@@ -1009,6 +1028,52 @@ void fa_fwd_h_kernel(Params p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
         };
+        // fp16 P at d = 64 (where the softmax bounds the kernel and the
+        // registers allow the scores to stay live while P is formed): P is
+        // formed against the trailing reference first, and the row maxima
+        // only when some P of the wave exceeds 2^lag or a row has no
+        // reference yet.  The test is a packed fp16 maximum over the P
+        // registers, half the instructions of the fp32 maximum over the
+        // scores.  Elsewhere the row maxima come first.
+        constexpr bool PFIRST = lag > 0.f && D == 64;
+        if constexpr (PFIRST) {
+            auto form_p = [&](float& ts) {
+                const float ref = (mc == -INFINITY) ? 0.f : mc;
+#pragma unroll
+                for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+                    for (int ps = 0; ps < 2; ++ps) {
+                        float pe[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            pe[e] = __builtin_amdgcn_exp2f(
+                                __builtin_fmaf(sacc[kt][8 * ps + e], FP8 ? ck[kt] : p.c, -ref));
+                            if constexpr (!LMMA) ts += pe[e];
+                        }
+                        pf[kt][ps] = Ty<T>::cvt(pe);
+                    }
+            };
+            float ts = 0.f;
+            form_p(ts);
+            if (__ballot(p16_above(pf, (_Float16)__builtin_exp2f(lag)) || mc == -INFINITY)) {
+                const float cand = row_max();
+                const bool bump = cand > mc;
+                const float alpha = bump ? __builtin_amdgcn_exp2f(mc - cand) : 1.f;
+                mc = bump ? cand : mc;
+                lsum *= alpha;
+                rescale(alpha);
+                if constexpr (LMMA) lacc[0] *= alpha;
+                ts = 0.f;
+                form_p(ts);
+            }
+            if constexpr (!LMMA) lsum += ts;
+            return;
+        }
+        // reference mc in scaled log2 units (-inf while no key is seen).  It
+        // trails the running max by at most lag: O and l are rescaled, and
+        // every row's mc brought up to its max, only in tiles where some row
+        // of the wave passed its mc by more than that
+        const float cand = row_max();
         if constexpr (lag > 0.f) {
             if (__ballot(cand > mc + lag)) {
                 const bool bump = cand > mc;
