@@ -92,14 +92,19 @@ SIMDS, ENGINE_GHZ = 1024, 2.4
 # at this rate, and at the engine clock measured under the counters, they
 # bound the kernel from below as well (the "one-wave issue bound").
 ONE_WAVE_VALU_CYCLES, ONE_WAVE_TRANS_CYCLES = 5.0, 8.7
+# The same wave's rates while the other wave of its SIMD issues MFMAs, as it
+# does through every softmax phase of the forward's ping-pong: 5.8 and 9.7
+# cycles (measured the same way, beside a wave running back-to-back
+# v_mfma_f32_32x32x16_bf16).
+MFMA_SIDE_VALU_CYCLES, MFMA_SIDE_TRANS_CYCLES = 5.8, 9.7
 
 
-def one_wave_bound_ms(waves, valu, trans, clock_ghz):
+def one_wave_bound_ms(waves, valu, trans, clock_ghz, rates=(ONE_WAVE_VALU_CYCLES, ONE_WAVE_TRANS_CYCLES)):
     """All waves' VALU work issued one wave per SIMD at a time at the one-wave
-    rates, in ms at `clock_ghz`; None without a clock figure."""
+    rates (or the given ones), in ms at `clock_ghz`; None without a clock figure."""
     if not clock_ghz:
         return None
-    cycles = (valu - trans) * ONE_WAVE_VALU_CYCLES + trans * ONE_WAVE_TRANS_CYCLES
+    cycles = (valu - trans) * rates[0] + trans * rates[1]
     return waves * cycles / (SIMDS * clock_ghz * 1e9) * 1e3
 
 
@@ -117,6 +122,8 @@ def valu_roofline(workload, ms_per_launch):
     cycles = (valu - trans) * VALU_CYCLES + trans * TRANS_CYCLES
     t_ms = w["waves"] * cycles / (SIMDS * ENGINE_GHZ * 1e9) * 1e3
     t1 = one_wave_bound_ms(w["waves"], valu, trans, w.get("engine_clock_ghz"))
+    t2 = one_wave_bound_ms(w["waves"], valu, trans, w.get("engine_clock_ghz"),
+                           (MFMA_SIDE_VALU_CYCLES, MFMA_SIDE_TRANS_CYCLES))
     return {
         "bound": "alu",
         "achieved": t_ms / ms_per_launch,
@@ -134,6 +141,11 @@ def valu_roofline(workload, ms_per_launch):
         "one_wave_model": f"the same VALU work issued one wave per SIMD at a time, {ONE_WAVE_VALU_CYCLES:g} / "
                           f"{ONE_WAVE_TRANS_CYCLES:g} cycles per instruction (measured one-wave rates), at the engine "
                           "clock measured under the counters",
+        "one_wave_beside_mfma_bound_ms": t2,
+        "one_wave_beside_mfma_frac": None if t2 is None else t2 / ms_per_launch,
+        "one_wave_beside_mfma_model": f"as the one-wave bound, at {MFMA_SIDE_VALU_CYCLES:g} / "
+                                      f"{MFMA_SIDE_TRANS_CYCLES:g} cycles per instruction (one wave's measured rates "
+                                      "while the other wave of its SIMD issues MFMAs)",
     }
 
 

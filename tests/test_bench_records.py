@@ -43,3 +43,19 @@ def test_records_match_sources_or_are_ignored(wl):
 def test_a_changed_source_voids_the_record(monkeypatch):
     monkeypatch.setattr(bench, "kernel_digest", lambda family="fwd": "0" * 64)
     assert bench.traffic_for("3") is None and bench.counters_for("3", 1.0) is None
+
+
+def test_valu_bounds_are_ordered():
+    """The three VALU issue bounds of a forward record: the chip-wide bound is
+    the loosest, one wave at a time the next, one wave beside an MFMA wave
+    (slower rates) the tightest; each is the counted instructions at its rates."""
+    w = bench._record("counters", "3")
+    if w is None:
+        pytest.skip("no counter record for the current forward source")
+    r = bench.valu_roofline("3", w["duration_ms_under_counters"])
+    assert r["frac"] < r["one_wave_frac"] < r["one_wave_beside_mfma_frac"]
+    pw = w["per_wave"]
+    valu, trans = pw["valu"] - pw["mfma"], pw["v_exp_f32"]
+    cyc = (valu - trans) * bench.MFMA_SIDE_VALU_CYCLES + trans * bench.MFMA_SIDE_TRANS_CYCLES
+    expect = w["waves"] * cyc / (bench.SIMDS * w["engine_clock_ghz"] * 1e9) * 1e3
+    assert r["one_wave_beside_mfma_bound_ms"] == pytest.approx(expect)
