@@ -131,7 +131,7 @@ size_t fa_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int nspli
  * k, v    : device, (B, H, Lk, d) in the same layout and type; read only.
  * lse     : device float32 (B, H, Lq); fully overwritten (natural log).
  * Lq      : query rows per (b, h), 1..8 (more rows: use fa_fwd).
- * Lk      : keys per (b, h), >= 1.  No mask: every query sees every key.
+ * Lk      : keys per (b, h), 1 .. 2^30.  No mask: every query sees every key.
  * d, scale, dtype : as for fa_fwd.
  * nsplit  : chunks per (b, h); <= 0 picks fa_splitkv_splits(B, H, Lk).
  *           Chunk s covers keys [s*c, min((s+1)*c, Lk)) with c = ceil(Lk/nsplit);

@@ -619,7 +619,7 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-    if ((long long)B * H * ((L + 127) / 128) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;   // one grid dimension
+    if ((long long)B * H * (((long long)L + 127) / 128) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;   // one grid dimension
     // per-head byte offsets go through 32-bit buffer descriptors
     if ((long long)L * d * 2 >= (1LL << 31)) return FA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||

@@ -1350,8 +1350,8 @@ extern "C" int fa_fwd_fp8(const void* q8, const void* k8, const float* q_scale, 
     p.ksc = k_scale;
     p.bq = block_q;
     p.bk = block_k;
-    p.nbq = (L + block_q - 1) / block_q;
-    p.nbk = (L + block_k - 1) / block_k;
+    p.nbq = (int)(((long long)L + block_q - 1) / block_q);
+    p.nbk = (int)(((long long)L + block_k - 1) / block_k);
     return dtype == FA_BF16 ? launch_fp8_t<__bf16>(p, d, causal, stream) : launch_fp8_t<_Float16>(p, d, causal, stream);
 }
 

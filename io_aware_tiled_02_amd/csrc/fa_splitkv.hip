@@ -310,7 +310,8 @@ int check_splitkv(const void* q, const void* k, const void* v, const void* o, co
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     int rc = check_common(B, H, Lq, d, dtype);
     if (rc != FA_OK) return rc;
-    if (Lk <= 0) return FA_ERR_INVALID_ARG;
+    // Lk up to 2^30 keeps the chunk bounds (split * chunk, key + 64) inside int
+    if (Lk <= 0 || Lk > (1 << 30)) return FA_ERR_INVALID_ARG;
     if (Lq > kMaxLq) return FA_ERR_UNSUPPORTED;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
     if ((long double)B * H * Lk * d >= 4.6e18L) return FA_ERR_INVALID_ARG;

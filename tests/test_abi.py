@@ -135,6 +135,8 @@ def _sk(**kw):
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
     (dict(B=300, H=300), fa.FA_ERR_INVALID_ARG),  # B*H over one grid dimension
     (dict(nsplit=4 * 65535 + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(Lk=(1 << 30) + 1), fa.FA_ERR_INVALID_ARG),   # chunk bounds must stay inside int
+    (dict(Lk=2 ** 31 - 1, nsplit=7), fa.FA_ERR_INVALID_ARG),
     (dict(q=A + 8), fa.FA_ERR_ALIGN),
     (dict(ws=W + 16), fa.FA_ERR_ALIGN),          # workspace must be 256-byte aligned
     (dict(wsz=1024), fa.FA_ERR_INVALID_ARG),      # workspace too small
@@ -231,6 +233,7 @@ def _bw(**kw):
     (dict(dtype=0), fa.FA_ERR_UNSUPPORTED),     # no fp32 backward
     (dict(B=65536, H=65536), fa.FA_ERR_INVALID_ARG),   # B*H*ceil(L/128) workgroups over one grid dimension
     (dict(L=1 << 23), fa.FA_ERR_INVALID_ARG),   # L*d*2 >= 2^31
+    (dict(L=2 ** 31 - 1), fa.FA_ERR_INVALID_ARG),   # no int overflow on the way to that answer
     (dict(dq=A + 8), fa.FA_ERR_ALIGN),
     (dict(lse=A + 2), fa.FA_ERR_ALIGN),
     (dict(ws=W + 64), fa.FA_ERR_ALIGN),
