@@ -32,6 +32,16 @@ def load():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it first (__graft_entry__.build())")
+        # PyTorch ships its own HIP runtime, which its libraries ask for by a
+        # file name other than the soname this library asks for.  Loaded
+        # first, this library would bring in the system runtime and torch
+        # then a second one, and torch's streams and memory would be foreign
+        # to this library's launches (FA_ERR_HIP).  With torch loaded first,
+        # both ask for the one runtime already in the process.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]

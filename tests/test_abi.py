@@ -302,3 +302,18 @@ def _f8(**kw):
 ])
 def test_fwd_fp8_argument_errors(kw, want):
     assert _f8(**kw) == want
+
+
+def test_one_hip_runtime_after_load():
+    """In a fresh process, loading the library through the binding before any
+    torch import leaves one HIP runtime mapped (torch's), not two: a second
+    runtime would make torch's streams foreign to the library's launches."""
+    import subprocess
+    import sys
+    code = ("import io_aware_tiled_02_amd as fa; fa.load(); import torch; "
+            "maps = open('/proc/self/maps').read().splitlines(); "
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1"
