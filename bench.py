@@ -564,7 +564,7 @@ def main():
                          "on this workload as child processes; write the summaries and records under profiles/")
     ap.add_argument("--summarize-counters", action="store_true",
                     help="only the summary step of --collect-counters, from raw output already under --prof-dir")
-    ap.add_argument("--prof-dir", default=os.path.join(ROOT, "gpurun_out", "prof"),
+    ap.add_argument("--prof-dir", default=os.path.join(ROOT, "prof_raw"),
                     help="where --collect-counters keeps rocprofv3's raw output")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"),
                     help="where the counter summaries and records are written")
@@ -757,7 +757,7 @@ def _rocprof(cmd_args, outdir, child, timeout_s):
            sys.executable, os.path.join(ROOT, "bench.py"), *child]
     env = dict(os.environ, TMPDIR="/tmp")
     shown = "cd /tmp && export TMPDIR=/tmp && " + " ".join(
-        c.replace(ROOT, "$GRAFT_REPO_ROOT").replace(sys.executable, "python3") for c in cmd)
+        c.replace(ROOT, "$REPO").replace(sys.executable, "python3") for c in cmd)
     print(f"[counters] {shown}", flush=True)
     res = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True, timeout=timeout_s)
     ok_line = any(l.startswith("{") for l in res.stdout.splitlines())
@@ -949,7 +949,7 @@ def summarize_counters(args):
     head = (f"Kernel source sha256 ({srcs}): `{sha}`\n\n"
             + "".join(f"Kernel: `{per[k]['name']}`\n\n" for k in spec["kernels"])
             + "Written by `python bench.py --collect-counters --workload " + wl + "` from the raw rocprofv3 output "
-            "of the commands below (run from the repository root on the MI355X box).\n")
+            "of the commands below ($REPO being the repository's path on the MI355X box).\n")
     md = [f"# {prefix}, {title} — kernel trace\n", head, "```", cmds["trace"], "```\n",
           "| kernel | calls | average (ns) | min (ns) | max (ns) | stddev (ns) | last timed calls (ns) | TFLOP/s there |",
           "|---|---|---|---|---|---|---|---|"]
